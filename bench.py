@@ -1,0 +1,212 @@
+"""Benchmark: gated triangle attention forward + backward on one MI355X.
+
+One step = tri_attn_fwd + tri_attn_bwd (starting node) at N=768, H=4, c=32,
+bf16 inputs/outputs with fp32 accumulation, on seeded synthetic inputs that are
+resident in HBM before timing starts.  Throughput uses the attention FLOP count
+14*N^3*H*c (forward 4, backward 10 per logit and channel: QK^T and PV forward;
+recomputed QK^T, dP, dV, dK, dQ backward).
+
+Prints ONE JSON line.  Stage and kernel durations are measured with HIP events
+recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tri-attn fwd+bwd TFLOP/s at N=768,H=4,c=32 bf16 (% of MFMA peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+class Hip:
+    """Minimal HIP event API through ctypes (events on the stream torch uses)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.lib.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(b) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "triangle_attention_tri_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches these sources."""
+    try:
+        with open(COUNTERS_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    k = d.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, rows: int):
+    """The fp64 oracle on `rows` rows (all heads, all queries and keys) of the same workload."""
+    import oracle
+    n, h, _, c = x["q"].shape
+    sel = slice(0, rows)
+    args = (x["q"][sel], x["k"][sel], x["v"][sel], x["bias"], x["gate"][sel], None, x["dout"][sel])
+    t0 = time.perf_counter()
+    r = oracle.attn_bwd(*args)
+    dt = time.perf_counter() - t0
+    flops = 14.0 * rows * n * n * h * c
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(r["threads"]), "kind": "oracle",
+            "sample": f"{rows} of {n} rows i (all {h} heads, all queries and keys), forward+backward, fp64, "
+                      f"{dt:.1f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--n", type=int, default=768)
+    ap.add_argument("--cpu-rows", type=int, default=128, help="rows of the oracle CPU sample (0 = skip)")
+    ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this single-GPU build",
+              file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+
+    import torch
+
+    import triangle_attention_tri_amd as ta
+    from triangle_attention_tri_amd import inputs
+
+    lib = ta.load()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    n, H, c = args.n, 4, 32
+    xc = inputs.attn_inputs(n, H, c, torch.bfloat16, seed=4)
+    xd = {k: (None if v is None else v.to(dev)) for k, v in xc.items()}
+    out = torch.empty_like(xd["gate"])
+    attn = torch.empty((n, H, n, c), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((n, H, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(xd[k]) for k in ("q", "k", "v"))
+    dbias, dgate = torch.empty_like(xd["bias"]), torch.empty_like(xd["gate"])
+    ws_bytes = ta.workspace_size(n, n, H, c, torch.bfloat16)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    bwd_events = (ctypes.c_void_p * 4)()
+    lib.tri_attn_bwd_profiled.argtypes = list(lib.tri_attn_bwd.argtypes) + [ctypes.c_void_p]
+    lib.tri_attn_bwd_profiled.restype = ctypes.c_int
+
+    def step(ending: int, ev=None):
+        if ev is not None:
+            hip.record(ev[0], stream)
+        st = lib.tri_attn_fwd(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
+                              P(xd["gate"]), None, P(out), P(attn), P(lse), stream)
+        assert st == 0, st
+        common = (n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]), P(xd["gate"]),
+                  None, P(attn), P(lse), P(xd["dout"]), P(dq), P(dk), P(dv), P(dbias), P(dgate), P(ws),
+                  ctypes.c_size_t(ws_bytes), stream)
+        if ev is None:
+            st = lib.tri_attn_bwd(*common)
+        else:
+            for i in range(4):
+                bwd_events[i] = ev[1 + i]
+            st = lib.tri_attn_bwd_profiled(*common, ctypes.cast(bwd_events, ctypes.c_void_p))
+        assert st == 0, st
+
+    def timed(ending: int, steps: int, warmup: int):
+        for _ in range(warmup):
+            step(ending)
+        torch.cuda.synchronize()
+        evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, stream)
+        for s in range(steps):
+            step(ending, evs[s])
+        hip.record(t1, stream)
+        torch.cuda.synchronize()
+        total = hip.ms(t0, t1)
+        stages = {"fwd": 0.0, "bwd_pre": 0.0, "bwd_main": 0.0, "dbias_reduce": 0.0}
+        for e in evs:
+            stages["fwd"] += hip.ms(e[0], e[1])
+            stages["bwd_pre"] += hip.ms(e[1], e[2])
+            stages["bwd_main"] += hip.ms(e[2], e[3])
+            stages["dbias_reduce"] += hip.ms(e[3], e[4])
+        return total / steps, {k: v / steps for k, v in stages.items()}
+
+    ms_step, stages = timed(0, args.steps, args.warmup)
+    flops = 14.0 * n ** 3 * H * c
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # roofline of the kernel that takes the most time
+    algo = {"fwd": ("mfma", 4.0 * n ** 3 * H * c), "bwd_main": ("mfma", 10.0 * n ** 3 * H * c),
+            "bwd_pre": ("hbm", None), "dbias_reduce": ("hbm", None)}
+    dom = max(("fwd", "bwd_main"), key=lambda k: stages[k])
+    bound, work = algo[dom]
+    achieved = work / (stages[dom] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    roofline = {"kernel": kernel_names[dom], "bound": bound, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(kernel_names[dom]), "launch_ms": round(stages[dom], 4)}
+
+    end_ms = None
+    if not args.no_end:
+        end_ms, _ = timed(1, max(3, args.steps // 2), 2)
+
+    cpu = None
+    if rank == 0 and args.cpu_rows > 0:
+        cpu = cpu_baseline(xc, min(args.cpu_rows, n))
+
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"tri_attn_start_fwd_bwd_N{n}_H{H}_c{c}_bf16", "n": n, "h": H, "c": c,
+                   "node": "start", "mask": None, "flops_per_step": flops},
+        "pct_of_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "end_node_ms_per_step": None if end_ms is None else round(end_ms, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if rank == 0:
+        print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

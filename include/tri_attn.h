@@ -1,0 +1,150 @@
+/*
+ * tri_attn.h — C ABI of the MI355X (gfx950) gated triangle self-attention
+ * library (libtri_attn.so).
+ *
+ * The operation (starting node).  The pages describe it in words: a pair
+ * representation attends, for each pair, over a third token, with a cost that
+ * grows cubically in the token count (TurboPairFormer news item, section
+ * "Dove si impiega il tempo"); the attention is gated (HelixFold review,
+ * "Fused Gated Self-Attention"); the N^2 x N interaction map is computed tile
+ * by tile in fast on-chip memory and never stored (MegaFold explainer,
+ * EvoFlash-3D paragraph).  Written out:
+ *
+ *   s[i,h,j,k] = q[i,h,j,:].k[i,h,k,:] / sqrt(c) + bias[h,j,k]
+ *                (-1e9 instead when mask[i,k] == 0)
+ *   a[i,h,j,:] = sum_k softmax_k(s[i,h,j,:]) v[i,h,k,:]
+ *   out[i,j,h,:] = sigmoid(gate[i,j,h,:]) * a[i,h,j,:]
+ *
+ * The backward recomputes each probability tile once and uses it for the
+ * query, key, value and pair-bias gradients (TurboPairFormer news item, same
+ * section); the pair-bias gradient is summed over rows i in a fixed order, so
+ * repeated calls give bit-identical results (same item, "Accuratezza e
+ * riproducibilità").
+ *
+ * Ending node (ending = 1): the same operation on the transposed pair layout,
+ * end = T o start o T, where T swaps the two pair axes.  The caller keeps its
+ * tensors in the ordinary pair layout; the kernels read and write them with the
+ * pair axes swapped, so no transpose pass is made.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    row-major, 16-byte aligned.  The library allocates nothing and keeps no
+ *    state besides cached kernel attributes.
+ *  - Element type of every tensor argument is `dtype` (TRI_ATTN_F32 or
+ *    TRI_ATTN_BF16) except mask (uint8, nonzero = keep), lse (fp32) and the
+ *    workspace (bytes).  bf16 runs accumulate in fp32.
+ *  - Only c == 32 is compiled (TRI_ATTN_EUNSUPPORTED otherwise).
+ *  - Rows: a call processes n_rows rows i (1 <= n_rows <= n) of an n x n pair
+ *    representation.  Pointers point at the first processed row.  Starting
+ *    node: q/k/v are [n_rows][h][n][c] and gate/out are [n_rows][n][h][c].
+ *    Ending node: q/k/v are the caller's [n][h][n][c] tensors and gate/out are
+ *    [n][n][h][c]; the processed rows i are along the SECOND pair axis, so the
+ *    pointer for row i0 is base + i0*c (q/k/v) or base + i0*h*c (gate/out) and
+ *    the mask pointer is base + i0.
+ *  - bias is [h][n][n]: bias[h][j][k] (starting node, query j, key k); for the
+ *    ending node the caller's bias[h][x][y] is read as bias[h][k][j].
+ *  - attn_saved [n_rows][h][n][c] (dtype) and lse [n_rows][h][n] (fp32,
+ *    natural-log log-sum-exp of each logit row) are written by the forward in
+ *    kernel row order for both nodes and must be passed unchanged to the
+ *    backward.
+ *  - Validation happens before any launch: on an error nothing is launched and
+ *    a negative status is returned.  Kernel launch failures return
+ *    TRI_ATTN_EHIP.  No call synchronises the stream; device faults surface at
+ *    the caller's next synchronisation.
+ *  - Calls are reentrant; calls on different streams with different buffers
+ *    may overlap.
+ */
+#ifndef TRI_ATTN_H
+#define TRI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *tri_attn_stream_t; /* same object as hipStream_t */
+typedef struct ihipEvent_t *tri_attn_event_t;   /* same object as hipEvent_t  */
+
+enum { TRI_ATTN_F32 = 0, TRI_ATTN_BF16 = 1 };
+
+enum {
+  TRI_ATTN_OK = 0,
+  TRI_ATTN_EINVAL = -1,       /* bad size, dtype, flag, null or misaligned pointer */
+  TRI_ATTN_EUNSUPPORTED = -2, /* valid but not compiled (c != 32, n too large)    */
+  TRI_ATTN_EWORKSPACE = -3,   /* workspace missing or smaller than required       */
+  TRI_ATTN_EHIP = -4          /* a HIP call or kernel launch failed               */
+};
+
+/* Library version (major*10000 + minor*100 + patch). */
+int tri_attn_version(void);
+
+/* Static text for a status code; never NULL. */
+const char *tri_attn_status_string(int status);
+
+/* Largest n the compiled kernels accept for a dtype (0 for a bad dtype). */
+int tri_attn_max_n(int dtype);
+
+/*
+ * Forward pass.
+ *   q, k, v     query/key/value, see conventions for the layout.
+ *   bias        [h][n][n] pair bias (un-scaled; 1/sqrt(c) applies to q.k only).
+ *   gate        gate pre-activation, same layout as out.
+ *   mask        [n_rows][n] key mask for each row (row stride n, key stride 1;
+ *               ending node: the caller's [n][n] mask read transposed), or NULL
+ *               for "every key kept".  A row whose keys are all masked gets
+ *               uniform weights over its n keys, as replacing every logit by
+ *               the same constant implies.
+ *   out         gated output.
+ *   attn_saved  pre-gate attention a, kept for the backward.
+ *   lse         log-sum-exp per logit row, kept for the backward.
+ */
+int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending,
+                 const void *q, const void *k, const void *v, const void *bias,
+                 const void *gate, const uint8_t *mask,
+                 void *out, void *attn_saved, float *lse, tri_attn_stream_t stream);
+
+/* Bytes of device workspace tri_attn_bwd needs for these sizes (0 on bad args). */
+size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype);
+
+/*
+ * Backward pass.  Inputs as for the forward plus attn_saved and lse from it and
+ * dout (gradient of out, same layout as out).  Outputs, all in dtype:
+ *   dq, dk, dv  same layouts as q, k, v.
+ *   dbias       [h][n][n] (same reading as bias), summed over the n_rows rows
+ *               of this call in ascending row-group order; overwritten.
+ *   dgate       gradient w.r.t. the gate pre-activation, same layout as gate.
+ * workspace     device scratch of at least tri_attn_bwd_workspace_size bytes,
+ *               256-byte aligned; its contents on entry do not matter.
+ * Results are bitwise identical across calls with the same inputs, sizes,
+ * device and library build.
+ */
+int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending,
+                 const void *q, const void *k, const void *v, const void *bias,
+                 const void *gate, const uint8_t *mask,
+                 const void *attn_saved, const float *lse, const void *dout,
+                 void *dq, void *dk, void *dv, void *dbias, void *dgate,
+                 void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
+
+/*
+ * tri_attn_bwd with per-stage timing: identical arguments and results, plus
+ * stage_events, an array of 4 caller-created HIP events recorded on `stream`
+ * before the gate/D preprocess, before the main backward kernel, before the
+ * pair-bias reduction and after it.  All four must be non-NULL
+ * (TRI_ATTN_EINVAL otherwise).  Intended for benchmarks that need the main
+ * kernel's own duration.
+ */
+int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending,
+                          const void *q, const void *k, const void *v, const void *bias,
+                          const void *gate, const uint8_t *mask,
+                          const void *attn_saved, const float *lse, const void *dout,
+                          void *dq, void *dk, void *dv, void *dbias, void *dgate,
+                          void *workspace, size_t workspace_bytes, tri_attn_stream_t stream,
+                          tri_attn_event_t *stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TRI_ATTN_H */

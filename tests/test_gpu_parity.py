@@ -1,0 +1,247 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar (normwise max|x - ref| / max|ref| per output tensor): 1e-4 for fp32 runs,
+2e-2 for bf16 inputs/outputs with fp32 accumulation.  Results must also be
+bitwise identical across repeated calls.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import triangle_attention_tri_amd as ta
+from triangle_attention_tri_amd import inputs
+from tests.helpers import assert_close, np64
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-4, torch.bfloat16: 2e-2}
+OUT_KEYS = ("out", "attn", "lse")
+GRAD_KEYS = ("dq", "dk", "dv", "dbias", "dgate")
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x, device):
+    return {k: (None if v is None else v.to(device)) for k, v in x.items()}
+
+
+def run_gpu(x, ending=False):
+    out, attn, lse = ta.fwd(x["q"], x["k"], x["v"], x["bias"], x["gate"], x["mask"], ending)
+    dq, dk, dv, dbias, dgate = ta.bwd(x["q"], x["k"], x["v"], x["bias"], x["gate"], x["mask"], attn, lse,
+                                      x["dout"], ending)
+    torch.cuda.synchronize()
+    return dict(out=out, attn=attn, lse=lse, dq=dq, dk=dk, dv=dv, dbias=dbias, dgate=dgate)
+
+
+# --- kernel-order views (rows i first) of caller tensors for either node -----
+def k_qkv(t, ending):   # caller [a,H,b,c] -> kernel [i,H,j,c]
+    return t.permute(2, 1, 0, 3) if ending else t
+
+
+def k_pair(t, ending):  # caller [a,b,H,c] -> kernel [i,j,H,c]
+    return t.permute(1, 0, 2, 3) if ending else t
+
+
+def k_bias(t, ending):  # caller [H,x,y] -> kernel [H,j,k]
+    return t.permute(0, 2, 1) if ending else t
+
+
+def k_mask(t, ending):
+    return None if t is None else (t.t() if ending else t)
+
+
+def oracle_rows(xc, rows, ending):
+    """Oracle forward+backward for the kernel rows `rows` (all queries, all keys)."""
+    q = k_qkv(xc["q"], ending)[rows]
+    k = k_qkv(xc["k"], ending)[rows]
+    v = k_qkv(xc["v"], ending)[rows]
+    gate = k_pair(xc["gate"], ending)[rows]
+    dout = k_pair(xc["dout"], ending)[rows]
+    bias = k_bias(xc["bias"], ending)
+    mask = k_mask(xc["mask"], ending)
+    mask = None if mask is None else mask[rows]
+    return oracle.attn_bwd(q, k, v, bias, gate, mask, dout)
+
+
+def oracle_dbias_queries(xc, qsel, ending):
+    """Exact dbias[:, qsel, :] (kernel order) summed over every row."""
+    q = k_qkv(xc["q"], ending)[:, :, qsel]
+    gate = k_pair(xc["gate"], ending)[:, qsel]
+    dout = k_pair(xc["dout"], ending)[:, qsel]
+    bias = k_bias(xc["bias"], ending)[:, qsel]
+    return oracle.attn_bwd(q, k_qkv(xc["k"], ending), k_qkv(xc["v"], ending), bias, gate,
+                           k_mask(xc["mask"], ending), dout)["dbias"]
+
+
+def gpu_rows(res, rows, ending):
+    g = {k: v.cpu() for k, v in res.items()}
+    return dict(out=k_pair(g["out"], ending)[rows], attn=g["attn"][rows], lse=g["lse"][rows],
+                dq=k_qkv(g["dq"], ending)[rows], dk=k_qkv(g["dk"], ending)[rows], dv=k_qkv(g["dv"], ending)[rows],
+                dgate=k_pair(g["dgate"], ending)[rows], dbias=k_bias(g["dbias"], ending))
+
+
+def check_full(name, xc, res, tol, ending=False):
+    n = xc["q"].shape[0]
+    rows = list(range(n))
+    ref = oracle_rows(xc, rows, ending)
+    got = gpu_rows(res, rows, ending)
+    errs = {}
+    for key in OUT_KEYS + GRAD_KEYS:
+        errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
+    log(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return errs
+
+
+def check_sampled(name, xc, res, tol, ending, rows, qsel):
+    ref = oracle_rows(xc, rows, ending)
+    got = gpu_rows(res, rows, ending)
+    errs = {}
+    for key in OUT_KEYS + ("dq", "dk", "dv", "dgate"):
+        errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
+    db_ref = oracle_dbias_queries(xc, qsel, ending)
+    errs["dbias"] = assert_close(f"{name}:dbias", got["dbias"][:, qsel], db_ref, tol)
+    log(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    return errs
+
+
+# --------------------------------------------------------------------------- workloads
+@pytest.mark.parametrize("widx", [0, 1, 2])
+def test_workload_full(device, widx):
+    w = inputs.WORKLOADS[widx]
+    log(f"workload {widx} {w.name}: full oracle comparison")
+    xc = inputs.workload_inputs(widx)
+    res = run_gpu(to_dev(xc, device))
+    check_full(w.name, xc, res, w.tol)
+
+
+@pytest.mark.parametrize("node", ["start", "end"])
+def test_workload3_sampled(device, node):
+    w = inputs.WORKLOADS[3]
+    log(f"workload 3 {w.name} node={node}: sampled rows / dbias queries")
+    xc = inputs.workload_inputs(3)
+    ending = node == "end"
+    res = run_gpu(to_dev(xc, device), ending)
+    n = w.n
+    rng = np.random.default_rng(3)
+    rows = sorted({0, 1, n // 2, n - 1, *rng.choice(n, 4, replace=False).tolist()})
+    qsel = sorted({0, 31, 32, n - 1, *rng.choice(n, 4, replace=False).tolist()})
+    check_sampled(f"{w.name}:{node}", xc, res, w.tol, ending, rows, qsel)
+
+
+@pytest.mark.parametrize("node", ["start", "end"])
+def test_attention_n768_sampled(device, node):
+    """Attention at the measured size (N=768, H=4, c=32, bf16), both nodes."""
+    log(f"attention n=768 node={node}: sampled rows / dbias queries")
+    xc = inputs.attn_inputs(768, 4, 32, torch.bfloat16, seed=4)
+    ending = node == "end"
+    res = run_gpu(to_dev(xc, device), ending)
+    rng = np.random.default_rng(4)
+    rows = sorted({0, 383, 767, *rng.choice(768, 3, replace=False).tolist()})
+    qsel = sorted({0, 767, *rng.choice(768, 4, replace=False).tolist()})
+    check_sampled(f"n768:{node}", xc, res, 2e-2, ending, rows, qsel)
+
+
+# --------------------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 33, 65, 127])
+def test_ragged_sizes(device, n, dtype):
+    log(f"ragged n={n} dtype={dtype}")
+    xc = inputs.attn_inputs(n, 4, 32, dtype, seed=100 + n, bias_std=1.5)
+    if n >= 3:
+        xc["mask"] = inputs.random_mask(n, seed=n, p_keep=0.7, full_rows=(1,))
+    res = run_gpu(to_dev(xc, device))
+    check_full(f"ragged{n}", xc, res, TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_ending_node_small(device, dtype):
+    n = 45
+    log(f"ending node n={n} dtype={dtype}")
+    xc = inputs.attn_inputs(n, 4, 32, dtype, seed=7, bias_std=2.0)
+    xc["mask"] = inputs.random_mask(n, seed=9, p_keep=0.8, full_rows=(4,))
+    res = run_gpu(to_dev(xc, device), ending=True)
+    check_full(f"end{n}", xc, res, TOL[dtype], ending=True)
+
+
+def test_row_slices(device):
+    """n_rows < n through the C ABI: a row slice gives that slice's outputs and dbias partial."""
+    n, h = 70, 4
+    log(f"row slices n={n}")
+    xc = inputs.attn_inputs(n, h, 32, torch.bfloat16, seed=11)
+    xd = to_dev(xc, device)
+    full = run_gpu(xd)
+    r0, r1 = 13, 50
+    sl = {k: (None if v is None else (v if k == "bias" else v[r0:r1].contiguous())) for k, v in xd.items()}
+    part = run_gpu(sl)
+    for key in ("out", "attn", "lse", "dq", "dk", "dv", "dgate"):
+        assert torch.equal(part[key], full[key][r0:r1]), key
+    ref = oracle.attn_bwd(xc["q"][r0:r1], xc["k"][r0:r1], xc["v"][r0:r1], xc["bias"], xc["gate"][r0:r1], None,
+                          xc["dout"][r0:r1])
+    assert_close("slice dbias", part["dbias"], ref["dbias"], 2e-2)
+
+
+def test_masked_keys_bitwise(device):
+    """Randomising k, v and bias at masked keys leaves every output bit-identical."""
+    n = 96
+    log("masked keys bitwise")
+    xc = inputs.attn_inputs(n, 4, 32, torch.bfloat16, seed=21)
+    mask = torch.ones((n, n), dtype=torch.uint8)
+    dead_keys = [5, 40, 41, 90]
+    mask[:, dead_keys] = 0
+    xc["mask"] = mask
+    base = run_gpu(to_dev(xc, device))
+    x2 = dict(xc)
+    g = torch.Generator().manual_seed(5)
+    for name in ("k", "v"):
+        t = x2[name].clone()
+        t[:, :, dead_keys] = torch.randn(t[:, :, dead_keys].shape, generator=g).to(t.dtype) * 10
+        x2[name] = t
+    b = x2["bias"].clone()
+    b[:, :, dead_keys] = torch.randn(b[:, :, dead_keys].shape, generator=g).to(b.dtype) * 10
+    x2["bias"] = b
+    res = run_gpu(to_dev(x2, device))
+    for key in ("out", "attn", "lse", "dq", "dgate"):
+        assert torch.equal(res[key], base[key]), key
+    assert torch.all(res["dk"][:, :, dead_keys] == 0) and torch.all(res["dv"][:, :, dead_keys] == 0)
+    assert torch.all(res["dbias"][:, :, dead_keys] == 0)
+
+
+def test_constant_values(device):
+    """V constant along keys: every softmax row sums to one, so attn equals that constant."""
+    n = 80
+    xc = inputs.attn_inputs(n, 4, 32, torch.float32, seed=31, bias_std=2.0)
+    u = torch.randn(32, generator=torch.Generator().manual_seed(1))
+    xc["v"] = u.expand(n, 4, n, 32).contiguous()
+    res = run_gpu(to_dev(xc, device))
+    err = (res["attn"].cpu() - u).abs().max().item()
+    assert err < 1e-5, err
+
+
+@pytest.mark.parametrize("widx", [1, 2])
+def test_determinism(device, widx):
+    """Five repeated calls give bitwise identical outputs and gradients."""
+    log(f"determinism workload {widx}")
+    xd = to_dev(inputs.workload_inputs(widx), device)
+    first = run_gpu(xd)
+    for rep in range(4):
+        again = run_gpu(xd)
+        for key in first:
+            assert torch.equal(first[key], again[key]), f"repeat {rep}: {key}"
+
+
+def test_determinism_n768(device):
+    log("determinism n=768 (5 runs)")
+    xd = to_dev(inputs.attn_inputs(768, 4, 32, torch.bfloat16, seed=4), device)
+    first = run_gpu(xd)
+    for rep in range(4):
+        again = run_gpu(xd)
+        for key in first:
+            assert torch.equal(first[key], again[key]), f"repeat {rep}: {key}"

@@ -1,0 +1,157 @@
+"""MI355X-native gated triangle self-attention with pair bias.
+
+Thin ctypes binding over ``libtri_attn.so`` (see ``include/tri_attn.h``):
+argument marshalling only, every step of the computation runs in the HIP
+kernels.  PyTorch provides device memory and the stream.
+
+    out, attn, lse = fwd(q, k, v, bias, gate, mask=None, ending=False)
+    dq, dk, dv, dbias, dgate = bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending=False)
+
+Layouts (starting node, N tokens, H heads, c = 32):
+    q, k, v [N,H,N,c]; bias [H,N,N]; gate, out, dout [N,N,H,c]; mask [N,N] uint8
+    (row i, key k; nonzero = keep) or None; attn [N,H,N,c]; lse [N,H,N] float32.
+With ``ending=True`` the same tensors are taken in the caller's pair layout and
+the operation runs around the ending node (the starting-node operation on the
+transposed pair layout).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["fwd", "bwd", "workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path", "load"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libtri_attn.so")
+_lib = None
+
+F32, BF16 = 0, 1
+_STATUS = {0: "ok", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "EWORKSPACE", -4: "EHIP"}
+
+
+def load():
+    """Load the HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise ImportError(f"{lib_path} is missing: build it with triangle_attention_tri_amd._build.build() "
+                          "(or __graft_entry__.build()); there is no fallback implementation")
+    lib = ctypes.CDLL(lib_path)
+    i, vp, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.tri_attn_version.restype = i
+    lib.tri_attn_status_string.argtypes = [i]
+    lib.tri_attn_status_string.restype = ctypes.c_char_p
+    lib.tri_attn_max_n.argtypes = [i]
+    lib.tri_attn_max_n.restype = i
+    lib.tri_attn_fwd.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tri_attn_fwd.restype = i
+    lib.tri_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.tri_attn_bwd_workspace_size.restype = sz
+    lib.tri_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
+    lib.tri_attn_bwd.restype = i
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().tri_attn_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: {_STATUS.get(status, status)} ({msg})")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dims(q, bias):
+    n_rows, h, n, c = q.shape
+    return n_rows, n, h, c
+
+
+def _prep(tensors, dtype, device):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def max_n(dtype) -> int:
+    import torch
+    return load().tri_attn_max_n(BF16 if dtype == torch.bfloat16 else F32)
+
+
+def workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:
+    import torch
+    return int(load().tri_attn_bwd_workspace_size(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def fwd(q, k, v, bias, gate, mask=None, ending: bool = False):
+    """Forward.  Returns (out, attn, lse)."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    n_rows, n, h, c = _dims(q, bias)
+    if ending:
+        n_rows = n
+    _prep(dict(q=q, k=k, v=v, bias=bias, gate=gate), q.dtype, q.device)
+    if mask is not None:
+        if mask.dtype != torch.uint8 or mask.device != q.device or not mask.is_contiguous():
+            raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    out = torch.empty_like(gate)
+    attn = torch.empty((n_rows, h, n, c), dtype=q.dtype, device=q.device)
+    lse = torch.empty((n_rows, h, n), dtype=torch.float32, device=q.device)
+    st = lib.tri_attn_fwd(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                          _ptr(gate), _ptr(mask), _ptr(out), _ptr(attn), _ptr(lse), _stream(q.device))
+    _check(st, "tri_attn_fwd")
+    return out, attn, lse
+
+
+def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, workspace=None):
+    """Backward.  Returns (dq, dk, dv, dbias, dgate)."""
+    import torch
+    lib = load()
+    dt = _dtype_code(q)
+    n_rows, n, h, c = _dims(q, bias)
+    if ending:
+        n_rows = n
+    _prep(dict(q=q, k=k, v=v, bias=bias, gate=gate, attn=attn, dout=dout), q.dtype, q.device)
+    need = int(lib.tri_attn_bwd_workspace_size(n_rows, n, h, c, dt))
+    if need == 0:
+        _check(-2 if c != 32 else -1, "tri_attn_bwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dbias, dgate = torch.empty_like(bias), torch.empty_like(gate)
+    st = lib.tri_attn_bwd(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                          _ptr(gate), _ptr(mask), _ptr(attn), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(dbias), _ptr(dgate), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                          _stream(q.device))
+    _check(st, "tri_attn_bwd")
+    return dq, dk, dv, dbias, dgate
+
+
+def __getattr__(name):
+    if name in ("TriAttnFunction", "tri_attn"):
+        from . import autograd as _ag
+        return getattr(_ag, name)
+    raise AttributeError(name)

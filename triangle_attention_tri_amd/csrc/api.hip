@@ -1,0 +1,223 @@
+// C ABI of libtri_attn.so: argument validation, layout strides for the
+// starting / ending node, workspace sizing and kernel dispatch.  Declared in
+// include/tri_attn.h.
+#include "../../include/tri_attn.h"
+#include "common.hpp"
+
+namespace tri {
+template <typename T, int R> hipError_t launch_fwd(const FwdArgs<T>&, hipStream_t);
+template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
+template <typename T, int R> size_t bwd_main_smem(int n);
+}  // namespace tri
+
+using namespace tri;
+
+namespace {
+
+constexpr size_t LDS_LIMIT = 160 * 1024;
+constexpr int FWD_R = 4;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Rows per backward workgroup: the largest compiled count whose LDS fits.
+// bf16 compiles 1, 2, 4 and fp32 1, 2 (larger counts spill registers).
+template <typename T> int pick_bwd_rows(int n);
+template <> int pick_bwd_rows<bf16>(int n) {
+  if (bwd_main_smem<bf16, 4>(n) <= LDS_LIMIT) return 4;
+  if (bwd_main_smem<bf16, 2>(n) <= LDS_LIMIT) return 2;
+  if (bwd_main_smem<bf16, 1>(n) <= LDS_LIMIT) return 1;
+  return 0;
+}
+template <> int pick_bwd_rows<float>(int n) {
+  if (bwd_main_smem<float, 2>(n) <= LDS_LIMIT) return 2;
+  if (bwd_main_smem<float, 1>(n) <= LDS_LIMIT) return 1;
+  return 0;
+}
+
+int pick_rows(int dtype, int n) {
+  return dtype == TRI_ATTN_BF16 ? pick_bwd_rows<bf16>(n) : pick_bwd_rows<float>(n);
+}
+
+int max_n(int dtype) {
+  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return 0;
+  int lo = 1, hi = 1 << 16;
+  if (pick_rows(dtype, lo) == 0) return 0;
+  while (lo < hi) {  // largest n with a fitting row count
+    int mid = lo + (hi - lo + 1) / 2;
+    if (pick_rows(dtype, mid) > 0) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(int n_rows, int n, int h, int c, int dtype, int ending) {
+  if (n_rows < 1 || n < 1 || h < 1 || n_rows > n) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return TRI_ATTN_EINVAL;
+  if (ending != 0 && ending != 1) return TRI_ATTN_EINVAL;
+  if (c != C) return TRI_ATTN_EUNSUPPORTED;
+  if ((long long)n * n * h > (1ll << 40)) return TRI_ATTN_EUNSUPPORTED;
+  if (n > max_n(dtype)) return TRI_ATTN_EUNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+Geo make_geo(int n_rows, int n, int h, int ending) {
+  Geo g;
+  g.n_rows = n_rows;
+  g.n = n;
+  g.H = h;
+  const long long hnc = (long long)h * n * C, hc = (long long)h * C;
+  if (!ending) {
+    g.qkv_row = hnc; g.qkv_pos = C;
+    g.pair_row = (long long)n * hc; g.pair_pos = hc;
+    g.bias_q = n; g.bias_k = 1;
+    g.mask_row = n; g.mask_key = 1;
+  } else {
+    g.qkv_row = C; g.qkv_pos = hnc;
+    g.pair_row = hc; g.pair_pos = (long long)n * hc;
+    g.bias_q = 1; g.bias_k = n;
+    g.mask_row = 1; g.mask_key = n;
+  }
+  return g;
+}
+
+struct WsLayout {
+  size_t dA, Dsum, slabs, total;
+  int rows, groups;
+};
+
+WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
+  WsLayout L{};
+  const size_t es = dtype == TRI_ATTN_BF16 ? 2 : 4;
+  L.rows = pick_rows(dtype, n);
+  if (L.rows == 0) return L;
+  L.groups = (n_rows + L.rows - 1) / L.rows;
+  L.dA = 0;
+  L.Dsum = align256(L.dA + (size_t)n_rows * h * n * C * es);
+  L.slabs = align256(L.Dsum + (size_t)n_rows * h * n * sizeof(float));
+  L.total = align256(L.slabs + (size_t)L.groups * h * n * n * sizeof(float));
+  return L;
+}
+
+template <typename T, int R> hipError_t launch_bwd_rows(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
+  if constexpr (sizeof(T) == 4 && R > 2) return hipErrorInvalidValue;
+  else return launch_bwd<T, R>(a, st, ev);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_EHIP; }
+
+template <typename T>
+int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const void* bias, const void* gate,
+           const uint8_t* mask, void* out, void* attn, float* lse, hipStream_t st) {
+  FwdArgs<T> a;
+  a.geo = geo;
+  a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v;
+  a.bias = (const T*)bias; a.gate = (const T*)gate; a.mask = mask;
+  a.out = (T*)out; a.attn = (T*)attn; a.lse = lse;
+  return hip_status(launch_fwd<T, FWD_R>(a, st));
+}
+
+template <typename T>
+int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, const void* v, const void* bias,
+           const void* gate, const uint8_t* mask, const void* attn, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, void* dbias, void* dgate, void* ws, hipStream_t st, hipEvent_t* ev) {
+  BwdArgs<T> a;
+  a.geo = geo;
+  a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v; a.bias = (const T*)bias;
+  a.gate = (const T*)gate; a.attn = (const T*)attn; a.dout = (const T*)dout;
+  a.mask = mask; a.lse = lse;
+  a.dq = (T*)dq; a.dk = (T*)dk; a.dv = (T*)dv; a.dbias = (T*)dbias; a.dgate = (T*)dgate;
+  char* base = (char*)ws;
+  a.dA = (T*)(base + L.dA);
+  a.Dsum = (float*)(base + L.Dsum);
+  a.slabs = (float*)(base + L.slabs);
+  a.groups = L.groups;
+  hipError_t e;
+  if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
+  else if (L.rows == 2) e = launch_bwd_rows<T, 2>(a, st, ev);
+  else if (L.rows == 1) e = launch_bwd_rows<T, 1>(a, st, ev);
+  else return TRI_ATTN_EUNSUPPORTED;
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_attn_version(void) { return 100; }
+
+const char* tri_attn_status_string(int status) {
+  switch (status) {
+    case TRI_ATTN_OK: return "ok";
+    case TRI_ATTN_EINVAL: return "invalid argument (size, dtype, flag, null or misaligned pointer)";
+    case TRI_ATTN_EUNSUPPORTED: return "unsupported configuration (only c == 32; n above the compiled maximum)";
+    case TRI_ATTN_EWORKSPACE: return "workspace missing or too small";
+    case TRI_ATTN_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tri_attn_max_n(int dtype) { return max_n(dtype); }
+
+int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                 const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
+                 void* attn_saved, float* lse, tri_attn_stream_t stream) {
+  int st = check_common(n_rows, n, h, c, dtype, ending);
+  if (st != TRI_ATTN_OK) return st;
+  const void* req[] = {q, k, v, bias, gate, out, attn_saved, lse};
+  for (const void* p : req)
+    if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
+  const Geo geo = make_geo(n_rows, n, h, ending);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == TRI_ATTN_BF16) return do_fwd<bf16>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, s);
+  return do_fwd<float>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, s);
+}
+
+size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
+  if (check_common(n_rows, n, h, c, dtype, 0) != TRI_ATTN_OK) return 0;
+  return ws_layout(n_rows, n, h, dtype).total;
+}
+
+static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                    const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
+                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate,
+                    void* workspace, size_t workspace_bytes, hipStream_t s, hipEvent_t* ev) {
+  int st = check_common(n_rows, n, h, c, dtype, ending);
+  if (st != TRI_ATTN_OK) return st;
+  const void* req[] = {q, k, v, bias, gate, attn_saved, lse, dout, dq, dk, dv, dbias, dgate};
+  for (const void* p : req)
+    if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
+  const WsLayout L = ws_layout(n_rows, n, h, dtype);
+  if (L.rows == 0) return TRI_ATTN_EUNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < L.total) return TRI_ATTN_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
+  const Geo geo = make_geo(n_rows, n, h, ending);
+  if (dtype == TRI_ATTN_BF16)
+    return do_bwd<bf16>(geo, L, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv, dbias, dgate,
+                        workspace, s, ev);
+  return do_bwd<float>(geo, L, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv, dbias, dgate,
+                       workspace, s, ev);
+}
+
+int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                 const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate,
+                 void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv,
+                  dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+}
+
+int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                          const void* v, const void* bias, const void* gate, const uint8_t* mask,
+                          const void* attn_saved, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                          void* dbias, void* dgate, void* workspace, size_t workspace_bytes,
+                          tri_attn_stream_t stream, tri_attn_event_t* stage_events) {
+  if (stage_events == nullptr) return TRI_ATTN_EINVAL;
+  for (int i = 0; i < 4; i++)
+    if (stage_events[i] == nullptr) return TRI_ATTN_EINVAL;
+  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv,
+                  dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, (hipEvent_t*)stage_events);
+}
+
+}  // extern "C"

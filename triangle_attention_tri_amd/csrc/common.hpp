@@ -1,0 +1,215 @@
+// Shared device-side definitions for the gfx950 triangle-attention kernels.
+//
+// Every contraction in the path is a 32 x 32 output tile with a contraction
+// length of 32 (the head dimension c, or a 32-wide block of queries or keys).
+// bf16 runs use v_mfma_f32_32x32x16_bf16 (two per contraction), fp32 runs use
+// v_mfma_f32_32x32x2_f32 (sixteen per contraction).  Both write the same
+// 32 x 32 fp32 accumulator layout: lane l, register r holds element
+//   row  m = (r & 3) + 4 * (l >> 5) + 8 * (r >> 2),   column n = l & 31.
+// For the A operand lane l supplies row m = l & 31, for the B operand column
+// n = l & 31; the contraction index a lane supplies depends only on its half
+// (l >> 5) and the element position, identically for A and B.  Two index maps
+// are used:
+//  * "c-map"  (both operands read from memory): bf16 element e of MFMA u in
+//    half g is index 16u + 8g + e; fp32 MFMA u in half g is index 2u + g.
+//  * "m-map"  (one operand is an accumulator tile reused as an operand): the
+//    element taken from accumulator register r covers index mrow(g, r), with
+//    r = 8u + e for bf16 and r = u for fp32.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tri {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int C = 32;             // head dimension (the only one compiled)
+constexpr int TILE = 32;          // queries / keys per tile
+constexpr float SQRT_C = 5.65685424949238019520f;      // sqrt(32)
+constexpr float INV_SQRT_C = 0.17677669529663688110f;  // 1/sqrt(32)
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float LN2 = 0.69314718055994530942f;
+constexpr float SC = LOG2E * INV_SQRT_C;  // raw logit -> log2 units
+constexpr float NEG_INF = -__builtin_huge_valf();
+constexpr float POS_INF = __builtin_huge_valf();
+constexpr float MASK_LOGIT = -1e9f;       // value a masked logit is replaced by
+
+__device__ __forceinline__ int mrow(int g, int r) { return (r & 3) + 4 * g + 8 * (r >> 2); }
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + fast_exp2(-x * LOG2E)); }
+
+// ---------------------------------------------------------------------------
+// MFMA traits
+template <typename T> struct MM;
+template <> struct MM<bf16> {
+  static constexpr int NU = 2;  // instructions per 32-long contraction
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MM<float> {
+  static constexpr int NU = 16;
+  typedef float frag;
+  static __device__ __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+template <typename T> struct Op { typename MM<T>::frag f[MM<T>::NU]; };
+
+template <typename T>
+__device__ __forceinline__ f32x16 mma32(const Op<T>& a, const Op<T>& b, f32x16 acc) {
+#pragma unroll
+  for (int u = 0; u < MM<T>::NU; u++) acc = MM<T>::mma(a.f[u], b.f[u], acc);
+  return acc;
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int r = 0; r < 16; r++) z[r] = 0.0f;
+  return z;
+}
+
+// c-map operand from a 32-element contiguous row (global or LDS).  Row must be
+// 16-byte aligned for bf16.
+__device__ __forceinline__ Op<bf16> load_c_op(const bf16* row, int g) {
+  Op<bf16> o;
+  o.f[0] = *reinterpret_cast<const bf16x8*>(row + 8 * g);
+  o.f[1] = *reinterpret_cast<const bf16x8*>(row + 16 + 8 * g);
+  return o;
+}
+__device__ __forceinline__ Op<float> load_c_op(const float* row, int g) {
+  Op<float> o;
+#pragma unroll
+  for (int u = 0; u < 16; u++) o.f[u] = row[2 * u + g];
+  return o;
+}
+template <typename T> __device__ __forceinline__ Op<T> zero_op() {
+  Op<T> o;
+#pragma unroll
+  for (int u = 0; u < MM<T>::NU; u++) o.f[u] = (typename MM<T>::frag)(0);
+  return o;
+}
+
+// m-map operand: element for contraction index k read from base[k * stride].
+template <typename T>
+__device__ __forceinline__ Op<T> load_m_op(const T* base, int stride, int g) {
+  Op<T> o;
+  if constexpr (MM<T>::NU == 2) {
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) o.f[u][e] = base[mrow(g, 8 * u + e) * stride];
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; u++) o.f[u] = base[mrow(g, u) * stride];
+  }
+  return o;
+}
+// m-map operand from a contiguous run (stride 1): bf16 uses two 8-byte reads per MFMA.
+__device__ __forceinline__ Op<bf16> load_m_op_contig(const bf16* base, int g) {
+  Op<bf16> o;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    bf16x4 lo = *reinterpret_cast<const bf16x4*>(base + 16 * u + 4 * g);
+    bf16x4 hi = *reinterpret_cast<const bf16x4*>(base + 16 * u + 8 + 4 * g);
+    o.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  return o;
+}
+__device__ __forceinline__ Op<float> load_m_op_contig(const float* base, int g) {
+  return load_m_op<float>(base, 1, g);
+}
+
+// accumulator tile -> m-map operand (rounded to T)
+template <typename T> __device__ __forceinline__ Op<T> acc_op(const f32x16& a);
+template <> __device__ __forceinline__ Op<bf16> acc_op<bf16>(const f32x16& a) {
+  Op<bf16> o;
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) o.f[u][e] = (bf16)a[8 * u + e];
+  return o;
+}
+template <> __device__ __forceinline__ Op<float> acc_op<float>(const f32x16& a) {
+  Op<float> o;
+#pragma unroll
+  for (int u = 0; u < 16; u++) o.f[u] = a[u];
+  return o;
+}
+
+// Store a c-map operand back as a contiguous 32-element row.
+__device__ __forceinline__ void store_c_op(bf16* row, const Op<bf16>& o, int g) {
+  *reinterpret_cast<bf16x8*>(row + 8 * g) = o.f[0];
+  *reinterpret_cast<bf16x8*>(row + 16 + 8 * g) = o.f[1];
+}
+__device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g) {
+#pragma unroll
+  for (int u = 0; u < 16; u++) row[2 * u + g] = o.f[u];
+}
+
+// 16-byte vector copy helpers for staging
+struct alignas(16) V16 { uint32_t w[4]; };
+
+// ---------------------------------------------------------------------------
+// Geometry shared by the kernels.  Element strides of the caller's tensors;
+// they encode the starting or ending node.
+struct Geo {
+  int n_rows, n, H;
+  long long qkv_row, qkv_pos;    // q, k, v, dq, dk, dv   (head stride n*C)
+  long long pair_row, pair_pos;  // gate, out, dout, dgate (head stride C)
+  long long bias_q, bias_k;      // bias, dbias            (head stride n*n)
+  long long mask_row, mask_key;  // mask
+};
+
+template <typename T> struct FwdArgs {
+  Geo geo;
+  const T *q, *k, *v, *bias, *gate;
+  const uint8_t* mask;
+  T *out, *attn;
+  float* lse;
+};
+
+template <typename T> struct BwdArgs {
+  Geo geo;
+  const T *q, *k, *v, *bias, *gate, *attn, *dout;
+  const uint8_t* mask;
+  const float* lse;
+  T *dq, *dk, *dv, *dbias, *dgate;
+  T* dA;           // workspace [n_rows][H][n][C], gradient reaching the pre-gate attention
+  float* Dsum;     // workspace [n_rows][H][n], D = sum_c dA * attn
+  float* slabs;    // workspace [groups][H][n][n] dbias partial per row group
+  int groups;
+};
+
+// Does row `row` keep at least one of its n keys?
+__device__ __forceinline__ bool row_has_valid_key(const uint8_t* mask, const Geo& g, int row, int lane) {
+  if (mask == nullptr) return true;
+  bool any = false;
+  for (int k = lane; k < g.n; k += 64) any |= mask[row * g.mask_row + k * g.mask_key] != 0;
+  return __ballot(any) != 0ull;
+}
+
+// Bit t set when key k0 + t (t < 32) of `row` is in range and kept.
+__device__ __forceinline__ uint32_t key_bits(const uint8_t* mask, const Geo& g, int row, int k0, int lane) {
+  int k = k0 + (lane & 31);
+  bool ok = k < g.n;
+  if (ok && mask != nullptr) ok = mask[row * g.mask_row + (long long)k * g.mask_key] != 0;
+  return (uint32_t)__ballot(ok);
+}
+
+}  // namespace tri

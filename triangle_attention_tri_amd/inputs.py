@@ -1,0 +1,85 @@
+"""Seeded synthetic inputs for the triangle-attention workloads.
+
+This module holds no arithmetic of the method: it only draws random tensors
+and builds masks, so the GPU path and the oracle can be fed the same values.
+
+Recipe (all on the CPU, one ``torch.Generator`` per call, seeded with the
+workload index):
+* draw order q, k, v, bias, gate, dout, each standard normal float32 in the
+  boundary layouts (q, k, v [N,H,N,c]; bias [H,N,N]; gate, dout [N,N,H,c]);
+* bias is multiplied by ``bias_std`` (2 for the wide-bias workload);
+* bf16 workloads round the float32 draws to bfloat16 (round to nearest even);
+  the oracle consumes the rounded values;
+* the key-padding workload keeps keys k < valid_len for every row i
+  (mask[i, k] = 1), i.e. the trailing tokens are padding.
+The sizes mirror the crops the pages train at (TurboPairFormer news item,
+"Benchmark di addestramento": crops 384, 640, 768) plus the AlphaFold2
+initial-training crop 256 and a small fp32 case; no dataset is involved.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    index: int
+    name: str
+    n: int
+    h: int = 4
+    c: int = 32
+    dtype: torch.dtype = torch.bfloat16
+    bias_std: float = 1.0
+    valid_len: int | None = None
+    nodes: tuple = ("start",)
+    block: bool = False
+    cz: int = 128
+    tol: float = 2e-2
+
+
+WORKLOADS = {
+    0: Workload(0, "start_n64_h4_c32_fp32", 64, dtype=torch.float32, tol=1e-4),
+    1: Workload(1, "start_n256_h4_c32_bf16", 256),
+    2: Workload(2, "start_n384_h4_c32_bf16_keymask345", 384, valid_len=345),
+    3: Workload(3, "start_end_n640_h4_c32_bf16_bias_std2", 640, bias_std=2.0, nodes=("start", "end")),
+    4: Workload(4, "block_start_end_n768_h4_c32_cz128_bf16", 768, nodes=("start", "end"), block=True),
+}
+
+
+def attn_inputs(n: int, h: int = 4, c: int = 32, dtype=torch.bfloat16, seed: int = 0,
+                bias_std: float = 1.0, valid_len: int | None = None) -> dict:
+    """Seeded attention inputs (CPU tensors).  See the module docstring."""
+    g = torch.Generator().manual_seed(int(seed))
+    q = torch.randn((n, h, n, c), generator=g)
+    k = torch.randn((n, h, n, c), generator=g)
+    v = torch.randn((n, h, n, c), generator=g)
+    bias = torch.randn((h, n, n), generator=g)
+    if bias_std != 1.0:
+        bias = bias * bias_std
+    gate = torch.randn((n, n, h, c), generator=g)
+    dout = torch.randn((n, n, h, c), generator=g)
+    out = dict(q=q, k=k, v=v, bias=bias, gate=gate, dout=dout)
+    if dtype != torch.float32:
+        out = {key: t.to(dtype) for key, t in out.items()}
+    mask = None
+    if valid_len is not None:
+        mask = torch.zeros((n, n), dtype=torch.uint8)
+        mask[:, :valid_len] = 1
+    out["mask"] = mask
+    return out
+
+
+def workload_inputs(index: int) -> dict:
+    w = WORKLOADS[index]
+    return attn_inputs(w.n, w.h, w.c, w.dtype, seed=w.index, bias_std=w.bias_std, valid_len=w.valid_len)
+
+
+def random_mask(n: int, seed: int, p_keep: float = 0.7, full_rows: tuple = ()) -> torch.Tensor:
+    """Random keep/drop mask [n, n] (uint8); rows listed in full_rows are all dropped."""
+    g = torch.Generator().manual_seed(int(seed))
+    m = (torch.rand((n, n), generator=g) < p_keep).to(torch.uint8)
+    for r in full_rows:
+        m[r, :] = 0
+    return m
