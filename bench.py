@@ -125,6 +125,8 @@ def main():
     dbias, dgate = torch.empty_like(xd["bias"]), torch.empty_like(xd["gate"])
     ws_bytes = ta.workspace_size(n, n, H, c, torch.bfloat16)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fws_bytes = ta.fwd_workspace_size(n, n, H, c, torch.bfloat16)
+    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
     bwd_events = (ctypes.c_void_p * 4)()
@@ -135,7 +137,7 @@ def main():
         if ev is not None:
             hip.record(ev[0], stream)
         st = lib.tri_attn_fwd(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
-                              P(xd["gate"]), None, P(out), P(attn), P(lse), stream)
+                              P(xd["gate"]), None, P(out), P(attn), P(lse), P(fws), ctypes.c_size_t(fws_bytes), stream)
         assert st == 0, st
         common = (n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]), P(xd["gate"]),
                   None, P(attn), P(lse), P(xd["dout"]), P(dq), P(dk), P(dv), P(dbias), P(dgate), P(ws),

@@ -86,6 +86,9 @@ const char *tri_attn_status_string(int status);
 /* Largest n the compiled kernels accept for a dtype (0 for a bad dtype). */
 int tri_attn_max_n(int dtype);
 
+/* Bytes of device workspace tri_attn_fwd needs for these sizes (0 on bad args). */
+size_t tri_attn_fwd_workspace_size(int n_rows, int n, int h, int c, int dtype);
+
 /*
  * Forward pass.
  *   q, k, v     query/key/value, see conventions for the layout.
@@ -99,11 +102,14 @@ int tri_attn_max_n(int dtype);
  *   out         gated output.
  *   attn_saved  pre-gate attention a, kept for the backward.
  *   lse         log-sum-exp per logit row, kept for the backward.
+ *   workspace   device scratch of at least tri_attn_fwd_workspace_size bytes,
+ *               256-byte aligned (holds the scaled bias tiles of this call).
  */
 int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending,
                  const void *q, const void *k, const void *v, const void *bias,
                  const void *gate, const uint8_t *mask,
-                 void *out, void *attn_saved, float *lse, tri_attn_stream_t stream);
+                 void *out, void *attn_saved, float *lse,
+                 void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
 
 /* Bytes of device workspace tri_attn_bwd needs for these sizes (0 on bad args). */
 size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype);
@@ -130,8 +136,8 @@ int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending,
 /*
  * tri_attn_bwd with per-stage timing: identical arguments and results, plus
  * stage_events, an array of 4 caller-created HIP events recorded on `stream`
- * before the gate/D preprocess, before the main backward kernel, before the
- * pair-bias reduction and after it.  All four must be non-NULL
+ * before the preprocessing kernels (gate gradient, D, scaled bias), before the
+ * main backward kernel, before the pair-bias reduction and after it.  All four must be non-NULL
  * (TRI_ATTN_EINVAL otherwise).  Intended for benchmarks that need the main
  * kernel's own duration.
  */

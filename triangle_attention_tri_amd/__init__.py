@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path", "load"]
+__all__ = ["fwd", "bwd", "workspace_size", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path", "load"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtri_attn.so")
@@ -44,7 +44,9 @@ def load():
     lib.tri_attn_status_string.restype = ctypes.c_char_p
     lib.tri_attn_max_n.argtypes = [i]
     lib.tri_attn_max_n.restype = i
-    lib.tri_attn_fwd.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.tri_attn_fwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.tri_attn_fwd_workspace_size.restype = sz
+    lib.tri_attn_fwd.argtypes = [i, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tri_attn_fwd.restype = i
     lib.tri_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.tri_attn_bwd_workspace_size.restype = sz
@@ -101,11 +103,17 @@ def max_n(dtype) -> int:
 
 
 def workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:
+    """Backward workspace bytes."""
     import torch
     return int(load().tri_attn_bwd_workspace_size(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
 
 
-def fwd(q, k, v, bias, gate, mask=None, ending: bool = False):
+def fwd_workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:
+    import torch
+    return int(load().tri_attn_fwd_workspace_size(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None):
     """Forward.  Returns (out, attn, lse)."""
     import torch
     lib = load()
@@ -117,11 +125,17 @@ def fwd(q, k, v, bias, gate, mask=None, ending: bool = False):
     if mask is not None:
         if mask.dtype != torch.uint8 or mask.device != q.device or not mask.is_contiguous():
             raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    need = int(lib.tri_attn_fwd_workspace_size(n_rows, n, h, c, dt))
+    if need == 0:
+        _check(-2 if c != 32 else -1, "tri_attn_fwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     out = torch.empty_like(gate)
     attn = torch.empty((n_rows, h, n, c), dtype=q.dtype, device=q.device)
     lse = torch.empty((n_rows, h, n), dtype=torch.float32, device=q.device)
     st = lib.tri_attn_fwd(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
-                          _ptr(gate), _ptr(mask), _ptr(out), _ptr(attn), _ptr(lse), _stream(q.device))
+                          _ptr(gate), _ptr(mask), _ptr(out), _ptr(attn), _ptr(lse), _ptr(workspace),
+                          ctypes.c_size_t(workspace.numel()), _stream(q.device))
     _check(st, "tri_attn_fwd")
     return out, attn, lse
 

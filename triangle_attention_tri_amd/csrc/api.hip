@@ -6,8 +6,11 @@
 
 namespace tri {
 template <typename T, int R> hipError_t launch_fwd(const FwdArgs<T>&, hipStream_t);
+size_t fwd_workspace_bytes(int n, int h);
 template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T, int R> size_t bwd_main_smem(int n);
+template <typename T, int KPW> hipError_t launch_bwd_tile(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
+template <typename T> size_t tile_smem(int kpw);
 }  // namespace tri
 
 using namespace tri;
@@ -15,7 +18,7 @@ using namespace tri;
 namespace {
 
 constexpr size_t LDS_LIMIT = 160 * 1024;
-constexpr int FWD_R = 4;
+constexpr int FWD_R = 2;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -82,20 +85,39 @@ Geo make_geo(int n_rows, int n, int h, int ending) {
   return g;
 }
 
+// Key tiles per wave of the per-row backward kernel (0: use the row-group kernel).
+int pick_kpw(int dtype, int n) {
+  const int nt = (n + TILE - 1) / TILE, kpw = (nt + 3) / 4;
+  const int max_kpw = dtype == TRI_ATTN_BF16 ? 6 : 2;
+  if (kpw > max_kpw) return 0;
+  const size_t smem = dtype == TRI_ATTN_BF16 ? tile_smem<bf16>(kpw) : tile_smem<float>(kpw);
+  return smem <= LDS_LIMIT ? kpw : 0;
+}
+
 struct WsLayout {
-  size_t dA, Dsum, slabs, total;
-  int rows, groups;
+  size_t dA, Dsum, slabs, bias_prep, tslab, total;
+  int rows, groups, kpw;
 };
 
 WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
   WsLayout L{};
   const size_t es = dtype == TRI_ATTN_BF16 ? 2 : 4;
+  const size_t nt = (size_t)(n + TILE - 1) / TILE;
+  L.kpw = pick_kpw(dtype, n);
+  L.dA = 0;
+  L.Dsum = align256(L.dA + (size_t)n_rows * h * n * C * es);
+  const size_t after_d = align256(L.Dsum + (size_t)n_rows * h * n * sizeof(float));
+  if (L.kpw > 0) {
+    L.rows = 1;
+    L.bias_prep = after_d;
+    L.tslab = align256(L.bias_prep + (size_t)h * nt * nt * 1024 * sizeof(float));
+    L.total = align256(L.tslab + (size_t)n_rows * h * nt * nt * 1024 * es);
+    return L;
+  }
   L.rows = pick_rows(dtype, n);
   if (L.rows == 0) return L;
   L.groups = (n_rows + L.rows - 1) / L.rows;
-  L.dA = 0;
-  L.Dsum = align256(L.dA + (size_t)n_rows * h * n * C * es);
-  L.slabs = align256(L.Dsum + (size_t)n_rows * h * n * sizeof(float));
+  L.slabs = after_d;
   L.total = align256(L.slabs + (size_t)L.groups * h * n * n * sizeof(float));
   return L;
 }
@@ -109,12 +131,13 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_E
 
 template <typename T>
 int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const void* bias, const void* gate,
-           const uint8_t* mask, void* out, void* attn, float* lse, hipStream_t st) {
+           const uint8_t* mask, void* out, void* attn, float* lse, void* ws, hipStream_t st) {
   FwdArgs<T> a;
   a.geo = geo;
   a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v;
   a.bias = (const T*)bias; a.gate = (const T*)gate; a.mask = mask;
   a.out = (T*)out; a.attn = (T*)attn; a.lse = lse;
+  a.bias_prep = (float*)ws;
   return hip_status(launch_fwd<T, FWD_R>(a, st));
 }
 
@@ -133,8 +156,24 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.Dsum = (float*)(base + L.Dsum);
   a.slabs = (float*)(base + L.slabs);
   a.groups = L.groups;
+  a.bias_prep = (float*)(base + L.bias_prep);
+  a.tslab = (T*)(base + L.tslab);
   hipError_t e;
-  if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
+  if (L.kpw > 0) {
+    switch (L.kpw) {
+      case 1: e = launch_bwd_tile<T, 1>(a, st, ev); break;
+      case 2: e = launch_bwd_tile<T, 2>(a, st, ev); break;
+      default:
+        if constexpr (sizeof(T) == 2) {
+          if (L.kpw == 3) e = launch_bwd_tile<T, 3>(a, st, ev);
+          else if (L.kpw == 4) e = launch_bwd_tile<T, 4>(a, st, ev);
+          else if (L.kpw == 5) e = launch_bwd_tile<T, 5>(a, st, ev);
+          else e = launch_bwd_tile<T, 6>(a, st, ev);
+        } else {
+          return TRI_ATTN_EUNSUPPORTED;
+        }
+    }
+  } else if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
   else if (L.rows == 2) e = launch_bwd_rows<T, 2>(a, st, ev);
   else if (L.rows == 1) e = launch_bwd_rows<T, 1>(a, st, ev);
   else return TRI_ATTN_EUNSUPPORTED;
@@ -160,18 +199,26 @@ const char* tri_attn_status_string(int status) {
 
 int tri_attn_max_n(int dtype) { return max_n(dtype); }
 
+size_t tri_attn_fwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
+  if (check_common(n_rows, n, h, c, dtype, 0) != TRI_ATTN_OK) return 0;
+  return align256(fwd_workspace_bytes(n, h));
+}
+
 int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
                  const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
-                 void* attn_saved, float* lse, tri_attn_stream_t stream) {
+                 void* attn_saved, float* lse, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
   int st = check_common(n_rows, n, h, c, dtype, ending);
   if (st != TRI_ATTN_OK) return st;
   const void* req[] = {q, k, v, bias, gate, out, attn_saved, lse};
   for (const void* p : req)
     if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
+  if (workspace == nullptr || workspace_bytes < align256(fwd_workspace_bytes(n, h))) return TRI_ATTN_EWORKSPACE;
+  if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
   const Geo geo = make_geo(n_rows, n, h, ending);
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == TRI_ATTN_BF16) return do_fwd<bf16>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, s);
-  return do_fwd<float>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, s);
+  if (dtype == TRI_ATTN_BF16)
+    return do_fwd<bf16>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, workspace, s);
+  return do_fwd<float>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, workspace, s);
 }
 
 size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
@@ -189,7 +236,7 @@ static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, cons
   for (const void* p : req)
     if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
   const WsLayout L = ws_layout(n_rows, n, h, dtype);
-  if (L.rows == 0) return TRI_ATTN_EUNSUPPORTED;
+  if (L.rows == 0 && L.kpw == 0) return TRI_ATTN_EUNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < L.total) return TRI_ATTN_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
   const Geo geo = make_geo(n_rows, n, h, ending);

@@ -1,0 +1,464 @@
+// Backward, one workgroup per (row i, head h) -- the path used up to n = 768.
+//
+// Each of the four waves owns every fourth 32-key tile of the row (up to six)
+// for the whole row: its V tiles sit in registers and its dK / dV
+// accumulators in accumulation registers, so dK and dV are complete when the
+// row ends and are written once.  K of the whole row sits in LDS (it is read
+// both as the logit operand and, transposed, as the dQ operand).  The query
+// tiles are walked in order; the next tile's Q and dA rows (and its
+// log-sum-exp and D values) are loaded into registers while the current one
+// is computed, then written to the other half of a double-buffered LDS area.
+// For every (query tile, key tile) the logit tile S = Q K^T + b and
+// P = exp(S - lse) are recomputed ONCE and feed all four gradients
+// (TurboPairFormer news item, "Dove si impiega il tempo"):
+//     dP - D = dA V^T - D     (D folded into the MFMA accumulator input)
+//     dS     = P (dP - D)
+//     dV^T  += dA^T P,   dK^T += Q^T dS,   dQ += dS K,   dbias partial = dS.
+// The tile is held as queries x keys (lane = key), so P and dS enter the dV
+// and dK products straight from the accumulator; dA^T and Q^T come from the
+// LDS copies through the gfx950 transposing read, and dS goes through a small
+// per-wave LDS tile to become the row operand of dQ.  dQ of a query tile is
+// the sum of the four waves' partials, added in wave order after one barrier.
+// The pair-bias gradient needs a sum over rows i, which no workgroup owns: each
+// row writes its dS tiles (in the operand precision, T) and a separate kernel
+// sums them over rows in ascending order in fp32.
+#include "common.hpp"
+
+namespace tri {
+
+template <typename T> constexpr int tpad() { return sizeof(T) == 2 ? 8 : 4; }
+
+template <typename T> struct TileSmem {
+  static constexpr int KP = TILE + tpad<T>();
+  static constexpr size_t tile = sizeof(T) * TILE * KP;
+  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)4 * kpw * tile; }  // K rows of the row
+  static constexpr size_t qd_bytes = 2 * 2 * tile;                           // Q, dA tiles x 2 buffers
+  static constexpr size_t ld_bytes = 2 * 2 * TILE * sizeof(float);           // lse*log2e, -D x 2 buffers
+  static constexpr size_t dt_bytes = 4 * tile;                               // per-wave dS^T tile
+  static constexpr size_t dq_bytes = 2 * 4 * 16 * 64 * sizeof(float);        // dQ partials x 2 buffers
+  static constexpr __host__ __device__ size_t total(int kpw) { return k_bytes(kpw) + qd_bytes + ld_bytes + dt_bytes + dq_bytes; }
+};
+
+// ---------------------------------------------------------------------------
+// gate backward + D, four threads per (row, query, head), eight channels each
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_pre_vec_kernel(BwdArgs<T> a) {
+  constexpr int EPT = 8;  // channels per thread
+  const Geo& G = a.geo;
+  const long long total = (long long)G.n_rows * G.n * G.H * 4;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const bool live = t < total;
+  const long long pr = live ? t >> 2 : 0;
+  const int part = (int)(t & 3);
+  const int h = (int)(pr % G.H);
+  const int j = (int)((pr / G.H) % G.n);
+  const int row = (int)(pr / ((long long)G.H * G.n));
+  const long long ip = row * G.pair_row + j * G.pair_pos + (long long)h * C + part * EPT;
+  const long long ia = (((long long)row * G.H + h) * G.n + j) * C + part * EPT;
+  float dsum = 0.0f;
+  if (live) {
+    float gt[EPT], dov[EPT], av[EPT], dg[EPT], da[EPT];
+#pragma unroll
+    for (int c = 0; c < EPT; c++) {
+      gt[c] = to_f(a.gate[ip + c]);
+      dov[c] = to_f(a.dout[ip + c]);
+      av[c] = to_f(a.attn[ia + c]);
+    }
+#pragma unroll
+    for (int c = 0; c < EPT; c++) {
+      const float sg = sigmoidf_(gt[c]);
+      da[c] = dov[c] * sg;
+      dg[c] = dov[c] * av[c] * sg * (1.0f - sg);
+      dsum += da[c] * av[c];
+    }
+#pragma unroll
+    for (int c = 0; c < EPT; c++) {
+      a.dgate[ip + c] = from_f<T>(dg[c]);
+      a.dA[ia + c] = from_f<T>(da[c]);
+    }
+  }
+  dsum += __shfl_xor(dsum, 1);
+  dsum += __shfl_xor(dsum, 2);
+  if (live && part == 0) a.Dsum[((long long)row * G.H + h) * G.n + j] = dsum;
+}
+
+// bias prep for the backward tile orientation (lane = key):
+// out[h][jt][kt][lane][r] = sqrt(c) * bias(j = jt*32 + mrow(lane>>5, r), k = kt*32 + (lane & 31))
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias, float* out) {
+  const int nt = (G.n + TILE - 1) / TILE;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long total = (long long)G.H * nt * nt * 64;
+  if (t >= total) return;
+  const int lane = (int)(t & 63);
+  const long long tile = t >> 6;
+  const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
+  const int k = kt * TILE + (lane & 31), g = lane >> 5;
+  f32x4 v[4];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int j = jt * TILE + mrow(g, r);
+    v[r >> 2][r & 3] = (j < G.n && k < G.n)
+                           ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C
+                           : 0.0f;
+  }
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+#pragma unroll
+  for (int q = 0; q < 4; q++) o[q] = v[q];
+}
+
+template <typename T>
+__device__ __forceinline__ f32x16 load_tile16(const float* base) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(base);
+  f32x16 v;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const f32x4 x = p[q];
+    v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
+  }
+  return v;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_tile_op(T* dst, const Op<T>& o);
+template <>
+__device__ __forceinline__ void store_tile_op<bf16>(bf16* dst, const Op<bf16>& o) {
+  reinterpret_cast<bf16x8*>(dst)[0] = o.f[0];
+  reinterpret_cast<bf16x8*>(dst)[1] = o.f[1];
+}
+template <>
+__device__ __forceinline__ void store_tile_op<float>(float* dst, const Op<float>& o) {
+  f32x4* d = reinterpret_cast<f32x4*>(dst);
+#pragma unroll
+  for (int q = 0; q < 4; q++) d[q] = (f32x4){o.f[4 * q], o.f[4 * q + 1], o.f[4 * q + 2], o.f[4 * q + 3]};
+}
+
+// dS (operand precision, accumulator order) -> per-wave LDS tile laid out [key][query]
+template <typename T>
+__device__ __forceinline__ void store_dst(T* tile, const Op<T>& o, int l32, int g);
+template <>
+__device__ __forceinline__ void store_dst<bf16>(bf16* tile, const Op<bf16>& o, int l32, int g) {
+  constexpr int KP = TileSmem<bf16>::KP;
+#pragma unroll
+  for (int s4 = 0; s4 < 4; s4++) {
+    const int u = s4 >> 1, e0 = 4 * (s4 & 1);
+    *reinterpret_cast<bf16x4*>(tile + l32 * KP + 8 * s4 + 4 * g) =
+        (bf16x4){o.f[u][e0], o.f[u][e0 + 1], o.f[u][e0 + 2], o.f[u][e0 + 3]};
+  }
+}
+template <>
+__device__ __forceinline__ void store_dst<float>(float* tile, const Op<float>& o, int l32, int g) {
+  constexpr int KP = TileSmem<float>::KP;
+#pragma unroll
+  for (int s4 = 0; s4 < 4; s4++)
+    *reinterpret_cast<f32x4*>(tile + l32 * KP + 8 * s4 + 4 * g) =
+        (f32x4){o.f[4 * s4], o.f[4 * s4 + 1], o.f[4 * s4 + 2], o.f[4 * s4 + 3]};
+}
+
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename T, int KPW>
+__global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
+  using SM = TileSmem<T>;
+  constexpr int KP = SM::KP;
+  constexpr int EPV = 16 / sizeof(T), CHUNKS = C / EPV;
+  constexpr int QLOADS = 2 * TILE * CHUNKS;            // Q and dA rows of one query tile
+  constexpr int QLPT = (QLOADS + 255) / 256;
+  extern __shared__ __align__(16) char smem[];
+  T* sK = reinterpret_cast<T*>(smem);
+  T* sQ = reinterpret_cast<T*>(smem + SM::k_bytes(KPW));                                   // [2][2][32][KP]
+  float* sLD = reinterpret_cast<float*>(smem + SM::k_bytes(KPW) + SM::qd_bytes);           // [2][2][32]
+  T* sDT = reinterpret_cast<T*>(smem + SM::k_bytes(KPW) + SM::qd_bytes + SM::ld_bytes);    // [4][32][KP]
+  float* sDQ = reinterpret_cast<float*>(smem + SM::k_bytes(KPW) + SM::qd_bytes + SM::ld_bytes + SM::dt_bytes);
+
+  const Geo& G = a.geo;
+  const int n = G.n, nt = (n + TILE - 1) / TILE;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int row = blockIdx.x, h = blockIdx.y;
+  const long long headq = (long long)h * n * C;
+  const long long irow = ((long long)row * G.H + h) * n;
+  const T* qrow = a.q + row * G.qkv_row + headq;
+  const bool degen = !row_has_valid_key(a.mask, G, row, lane);
+  const float inv_n = fast_exp2(-__log2f((float)n));
+  T* wdt = sDT + w * TILE * KP;
+
+  // K of the whole row into LDS (row-major, key tiles back to back)
+  for (int idx = tid; idx < nt * TILE * CHUNKS; idx += 256) {
+    const int key = idx / CHUNKS, ch = idx % CHUNKS;
+    V16 val = {{0u, 0u, 0u, 0u}};
+    if (key < n) val = *reinterpret_cast<const V16*>(a.k + row * G.qkv_row + headq + key * G.qkv_pos + ch * EPV);
+    *reinterpret_cast<V16*>(sK + key * KP + ch * EPV) = val;
+  }
+  // this wave's V tiles (B operand of dA V^T, lane = key) and key masks
+  Op<T> vb[KPW];
+  uint32_t kbits[KPW];
+  f32x16 dkt[KPW], dvt[KPW];
+#pragma unroll
+  for (int t = 0; t < KPW; t++) {
+    const int kk = (t * 4 + w) * TILE + l32;
+    vb[t] = kk < n ? load_c_op(a.v + row * G.qkv_row + headq + kk * G.qkv_pos, g) : zero_op<T>();
+    kbits[t] = key_bits(a.mask, G, row, (t * 4 + w) * TILE, lane);
+    dkt[t] = zero16();
+    dvt[t] = zero16();
+  }
+
+  // query-tile staging
+  V16 qpre[QLPT];
+  f32x4 ldpre = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto issue_q = [&](int jt) {
+#pragma unroll
+    for (int q = 0; q < QLPT; q++) {
+      const int idx = tid + 256 * q;
+      qpre[q] = V16{{0u, 0u, 0u, 0u}};
+      if (idx < QLOADS) {
+        const int which = idx / (TILE * CHUNKS), jr = (idx / CHUNKS) % TILE, ch = idx % CHUNKS;
+        const int jj = jt * TILE + jr;
+        if (jj < n)
+          qpre[q] = *reinterpret_cast<const V16*>(which ? a.dA + (irow + jj) * C + ch * EPV
+                                                        : qrow + jj * G.qkv_pos + ch * EPV);
+      }
+    }
+    if (tid < 16) {
+      const int which = tid >> 3, j0 = jt * TILE + 4 * (tid & 7);
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const int jj = j0 + t;
+        ldpre[t] = which == 0 ? (jj < n ? a.lse[irow + jj] * LOG2E : POS_INF) : (jj < n ? -a.Dsum[irow + jj] : 0.0f);
+      }
+    }
+  };
+  auto stash_q = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < QLPT; q++) {
+      const int idx = tid + 256 * q;
+      if (idx < QLOADS) {
+        const int which = idx / (TILE * CHUNKS), jr = (idx / CHUNKS) % TILE, ch = idx % CHUNKS;
+        *reinterpret_cast<V16*>(sQ + ((buf * 2 + which) * TILE + jr) * KP + ch * EPV) = qpre[q];
+      }
+    }
+    if (tid < 16) *reinterpret_cast<f32x4*>(sLD + (buf * 2 + (tid >> 3)) * TILE + 4 * (tid & 7)) = ldpre;
+  };
+
+  const float* bp_row = a.bias_prep + (long long)h * nt * nt * 1024 + lane * 16;
+  issue_q(0);
+  stash_q(0);
+  f32x16 bnext = (w < nt) ? load_tile16<T>(bp_row + (long long)w * 1024) : zero16();
+  __syncthreads();
+
+  for (int jt = 0; jt < nt; jt++) {
+    const int b = jt & 1;
+    if (jt + 1 < nt) issue_q(jt + 1);
+    const T* tq = sQ + (b * 2 + 0) * TILE * KP;
+    const T* tda = sQ + (b * 2 + 1) * TILE * KP;
+    const Op<T> qa = lds_c_op(tq + l32 * KP, g);
+    const Op<T> daa = lds_c_op(tda + l32 * KP, g);
+    float lse2[16];
+    f32x16 dng;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sLD + (b * 2 + 0) * TILE + 8 * s4 + 4 * g);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sLD + (b * 2 + 1) * TILE + 8 * s4 + 4 * g);
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        lse2[4 * s4 + t] = l4[t];
+        dng[4 * s4 + t] = d4[t];
+      }
+    }
+    f32x16 dq = zero16();
+    const float* bp_jt = bp_row + (long long)jt * nt * 1024;
+#pragma unroll
+    for (int t = 0; t < KPW; t++) {
+      const int kt = t * 4 + w;
+      if (kt >= nt) break;
+      const f32x16 bcur = bnext;
+      if (kt + 4 < nt) bnext = load_tile16<T>(bp_jt + (long long)(kt + 4) * 1024);
+      else if (jt + 1 < nt && w < nt) bnext = load_tile16<T>(bp_jt + (long long)nt * 1024 + (long long)w * 1024);
+      const T* tk = sK + kt * TILE * KP;
+      const Op<T> kb = lds_c_op(tk + l32 * KP, g);
+      const f32x16 s = mma32(qa, kb, bcur);        // [query j0+mrow(g,r)][key kt*32+l32], raw units
+      f32x16 p, ds;
+      if (degen) {
+        const bool kin = kt * TILE + l32 < n;
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          p[r] = (kin && lse2[r] != POS_INF) ? inv_n : 0.0f;
+          ds[r] = 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], SC, -lse2[r]));
+        if (kbits[t] != 0xffffffffu) {
+          const bool kv = (kbits[t] >> l32) & 1u;
+#pragma unroll
+          for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
+        }
+      }
+      const f32x16 dp = mma32(daa, vb[t], dng);    // dP - D
+      if (!degen) {
+#pragma unroll
+        for (int r = 0; r < 16; r++) ds[r] = p[r] * dp[r];
+      }
+      const Op<T> pb = acc_op<T>(p);
+      const Op<T> dsb = acc_op<T>(ds);
+      const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
+      dvt[t] = mma32(dat, pb, dvt[t]);             // [channel][key]
+      const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
+      dkt[t] = mma32(qt, dsb, dkt[t]);             // [channel][key]
+      store_dst<T>(wdt, dsb, l32, g);
+      wave_sync_lds();
+      const Op<T> dsa = lds_tr_op<MAP_C>(wdt, KP, lane);   // row = query, contraction = key
+      const Op<T> ktb = lds_tr_op<MAP_C>(tk, KP, lane);    // column = channel, contraction = key
+      dq = mma32(dsa, ktb, dq);                    // [query][channel]
+      store_tile_op<T>(a.tslab + ((((long long)row * G.H + h) * nt + jt) * nt + kt) * 1024 + lane * 16, dsb);
+      wave_sync_lds();
+    }
+    float* slot = sDQ + (b * 4 + w) * 16 * 64 + lane;
+#pragma unroll
+    for (int r = 0; r < 16; r++) slot[r * 64] = dq[r];
+    if (jt + 1 < nt) stash_q(b ^ 1);
+    __syncthreads();
+    {
+      const int r = tid >> 4, l0 = 4 * (tid & 15);
+      f32x4 sum = *reinterpret_cast<const f32x4*>(sDQ + ((b * 4 + 0) * 16 + r) * 64 + l0);
+#pragma unroll
+      for (int ww = 1; ww < 4; ww++) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sDQ + ((b * 4 + ww) * 16 + r) * 64 + l0);
+        sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
+      }
+      const int jj = jt * TILE + mrow(l0 >> 5, r), c0 = l0 & 31;
+      if (jj < n) {
+        T* dst = a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0;
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(sum[0] * INV_SQRT_C), (bf16)(sum[1] * INV_SQRT_C),
+                                                     (bf16)(sum[2] * INV_SQRT_C), (bf16)(sum[3] * INV_SQRT_C)};
+        else
+          *reinterpret_cast<f32x4*>(dst) = (f32x4){sum[0] * INV_SQRT_C, sum[1] * INV_SQRT_C, sum[2] * INV_SQRT_C,
+                                                   sum[3] * INV_SQRT_C};
+      }
+    }
+  }
+
+  // dK and dV of this wave's key tiles
+#pragma unroll
+  for (int t = 0; t < KPW; t++) {
+    const int kk = (t * 4 + w) * TILE + l32;
+    if (kk >= n) continue;
+    const long long off = row * G.qkv_row + headq + kk * G.qkv_pos;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      const int c0 = 4 * g + 8 * s4;
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<bf16x4*>(a.dk + off + c0) =
+            (bf16x4){(bf16)(dkt[t][4 * s4] * INV_SQRT_C), (bf16)(dkt[t][4 * s4 + 1] * INV_SQRT_C),
+                     (bf16)(dkt[t][4 * s4 + 2] * INV_SQRT_C), (bf16)(dkt[t][4 * s4 + 3] * INV_SQRT_C)};
+        *reinterpret_cast<bf16x4*>(a.dv + off + c0) =
+            (bf16x4){(bf16)dvt[t][4 * s4], (bf16)dvt[t][4 * s4 + 1], (bf16)dvt[t][4 * s4 + 2], (bf16)dvt[t][4 * s4 + 3]};
+      } else {
+        *reinterpret_cast<f32x4*>(a.dk + off + c0) =
+            (f32x4){dkt[t][4 * s4] * INV_SQRT_C, dkt[t][4 * s4 + 1] * INV_SQRT_C, dkt[t][4 * s4 + 2] * INV_SQRT_C,
+                    dkt[t][4 * s4 + 3] * INV_SQRT_C};
+        *reinterpret_cast<f32x4*>(a.dv + off + c0) =
+            (f32x4){dvt[t][4 * s4], dvt[t][4 * s4 + 1], dvt[t][4 * s4 + 2], dvt[t][4 * s4 + 3]};
+      }
+    }
+  }
+}
+
+// dbias[h][j][k] = sum over rows (ascending) of the per-row dS tiles, fp32.
+// One thread per (h, jt, kt, lane, group of 4 registers).
+template <typename T>
+__global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
+  const Geo& G = a.geo;
+  const int n = G.n, nt = (n + TILE - 1) / TILE;
+  const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per row of tiles
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= per_row / 4) return;
+  const long long e0 = t * 4;  // first element: [h][jt][kt][lane][r0..r0+3]
+  const int r0 = (int)(e0 & 15), lane = (int)((e0 >> 4) & 63);
+  const long long tile = e0 >> 10;
+  const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
+  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  const T* src = a.tslab + e0;
+  int row = 0;
+  for (; row + 4 <= G.n_rows; row += 4) {
+    float v[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      if constexpr (sizeof(T) == 2) {
+        const bf16x4 x = *reinterpret_cast<const bf16x4*>(src + (row + q) * per_row);
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[q][i] = (float)x[i];
+      } else {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (row + q) * per_row);
+#pragma unroll
+        for (int i = 0; i < 4; i++) v[q][i] = x[i];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) s[i] += v[q][i];
+  }
+  for (; row < G.n_rows; row++) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) s[i] += to_f(src[row * per_row + i]);
+  }
+  const int k = kt * TILE + (lane & 31), g = lane >> 5;
+  if (k >= n) return;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int j = jt * TILE + mrow(g, r0 + i);
+    if (j < n) a.dbias[(long long)h * n * n + j * G.bias_q + k * G.bias_k] = from_f<T>(s[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <typename T> size_t tile_smem(int kpw) { return TileSmem<T>::total(kpw); }
+
+template <typename T, int KPW>
+hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
+  const Geo& G = a.geo;
+  const int nt = (G.n + TILE - 1) / TILE;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  const long long pre_threads = (long long)G.n_rows * G.n * G.H * 4;
+  hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long prep_threads = (long long)G.H * nt * nt * 64;
+  hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
+                     a.bias, a.bias_prep);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)bwd_tile_kernel<T, KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(G.n_rows, G.H), dim3(256), TileSmem<T>::total(KPW), st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  const long long red_threads = (long long)G.H * nt * nt * 256;
+  hipLaunchKernelGGL((dbias_tile_reduce_kernel<T>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template hipError_t launch_bwd_tile<bf16, 1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<bf16, 2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<bf16, 3>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<bf16, 4>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<bf16, 5>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<bf16, 6>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<float, 1>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile<float, 2>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
+template size_t tile_smem<bf16>(int);
+template size_t tile_smem<float>(int);
+
+}  // namespace tri

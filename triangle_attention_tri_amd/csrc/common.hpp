@@ -166,6 +166,87 @@ __device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g
 struct alignas(16) V16 { uint32_t w[4]; };
 
 // ---------------------------------------------------------------------------
+// Operands read from row-major LDS tiles (32 rows, `pitch` elements per row).
+//
+// lds_c_op: the lane's row/column index is the LDS ROW (lane & 31) and the
+// contraction runs along the row (c-map) -- a plain vector read.
+//
+// lds_tr_op: the lane's row/column index is the LDS COLUMN (lane & 31) and the
+// contraction runs down the rows.  bf16 uses the gfx950 transposing read
+// ds_read_b64_tr_b16: inside each 16-lane group, lane i receives element i%4
+// of the 8-byte vectors addressed by lanes i/4 + 4e (e = 0..3), so if lane
+// j of the group addresses row base+j/4, columns 4(j%4)..+3, lane i gets
+// column i of rows base..base+3.  fp32 uses scalar reads with the same map.
+// MAP selects which contraction index each element carries:
+//   MAP_M: element (u, e) <-> row mrow(g, 8u+e)   (pairs with acc_op operands)
+//   MAP_C: element (u, e) <-> row 16u + 8g + e    (pairs with other LDS/c-map operands)
+enum { MAP_M = 0, MAP_C = 1 };
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+  typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+  v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ Op<bf16> lds_c_op(const bf16* row, int g) { return load_c_op(row, g); }
+__device__ __forceinline__ Op<float> lds_c_op(const float* row, int g) { return load_c_op(row, g); }
+
+template <int MAP>
+__device__ __forceinline__ int tr_row(int u, int half, int g) {
+  return MAP == MAP_M ? 16 * u + 8 * half + 4 * g : 16 * u + 8 * g + 4 * half;
+}
+
+template <int MAP>
+__device__ __forceinline__ Op<bf16> lds_tr_op(const bf16* tile, int pitch, int lane) {
+  const int G = lane >> 4, jp = lane & 15, g = lane >> 5;
+  const bf16* base = tile + (jp >> 2) * pitch + 16 * (G & 1) + 4 * (jp & 3);
+  Op<bf16> o;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const bf16x4 lo = lds_read_tr(base + tr_row<MAP>(u, 0, g) * pitch);
+    const bf16x4 hi = lds_read_tr(base + tr_row<MAP>(u, 1, g) * pitch);
+    o.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  return o;
+}
+template <int MAP>
+__device__ __forceinline__ Op<float> lds_tr_op(const float* tile, int pitch, int lane) {
+  const int g = lane >> 5, col = lane & 31;
+  Op<float> o;
+#pragma unroll
+  for (int u = 0; u < 16; u++) {
+    const int row = MAP == MAP_M ? mrow(g, u) : 2 * u + g;
+    o.f[u] = tile[row * pitch + col];
+  }
+  return o;
+}
+
+// Sum of the 16 rounded probabilities a lane holds, from the bf16 operand
+// (v_dot2_f32_bf16 against ones: two products per instruction).
+__device__ __forceinline__ float op_sum(const Op<bf16>& o) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 4) {
+      s0 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){o.f[u][e], o.f[u][e + 1]}, one, s0, false);
+      s1 = __builtin_amdgcn_fdot2_f32_bf16((bf16x2){o.f[u][e + 2], o.f[u][e + 3]}, one, s1, false);
+    }
+  }
+  return s0 + s1;
+}
+__device__ __forceinline__ float op_sum(const Op<float>& o) {
+  float s = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 16; u++) s += o.f[u];
+  return s;
+}
+
+// ---------------------------------------------------------------------------
 // Geometry shared by the kernels.  Element strides of the caller's tensors;
 // they encode the starting or ending node.
 struct Geo {
@@ -182,6 +263,7 @@ template <typename T> struct FwdArgs {
   const uint8_t* mask;
   T *out, *attn;
   float* lse;
+  float* bias_prep;  // workspace: sqrt(c)-scaled bias in per-lane tile order
 };
 
 template <typename T> struct BwdArgs {
@@ -192,8 +274,10 @@ template <typename T> struct BwdArgs {
   T *dq, *dk, *dv, *dbias, *dgate;
   T* dA;           // workspace [n_rows][H][n][C], gradient reaching the pre-gate attention
   float* Dsum;     // workspace [n_rows][H][n], D = sum_c dA * attn
-  float* slabs;    // workspace [groups][H][n][n] dbias partial per row group
+  float* slabs;    // workspace [groups][H][n][n] dbias partial per row group (row-group kernel)
   int groups;
+  float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order
+  T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
 };
 
 // Does row `row` keep at least one of its n keys?

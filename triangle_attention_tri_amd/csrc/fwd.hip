@@ -1,139 +1,204 @@
-// Forward kernel: logits + pair bias + mask, online softmax, P.V, sigmoid gate.
+// Forward: logits + pair bias + mask, online softmax, P.V, sigmoid gate.
 //
-// Work split.  A workgroup of four waves takes R consecutive rows i of one
-// head h and 128 consecutive queries j (32 per wave).  It walks the keys in
-// tiles of 32: each tile's K rows and transposed V rows of the R rows are
-// staged in LDS once and shared by the four waves.  A wave keeps, per row, the
-// running max, running sum and the 32 x 32 output accumulator in registers and
-// computes the logit tile transposed (keys x queries), so each lane owns one
-// query and the softmax max over a tile is a register reduction plus one swap
-// between the two 32-lane halves.  The pair-bias tile of the wave's queries is
-// loaded and scaled once per key tile and reused for all R rows (the bias does
-// not depend on i), and is fed to the logit MFMA as its accumulator input.
+// Work split.  A workgroup of four waves takes R consecutive rows i of one head
+// h and 128 consecutive queries j (32 per wave); two workgroups share a CU.  It
+// walks the keys in tiles of 32.  The K and V rows of the next tile are loaded
+// from HBM into registers while the current tile is computed, then written to
+// the other half of a double-buffered LDS area, so there is one barrier per
+// key tile.  The logit tile is computed transposed (keys x queries): each lane
+// owns one query and 16 of the tile's keys, the other lane half owns the other
+// 16.  The pair-bias tile is fed to the logit MFMA as its accumulator input and
+// shared by the R rows (the bias does not depend on i); a prep kernel writes
+// it once per call, pre-scaled by sqrt(c) in fp32, in exactly the register
+// order a lane needs, so the main loop spends no VALU on it.
 //
-// Scaling.  The MFMA produces raw = q.k + sqrt(c)*b = sqrt(c)*s; the softmax
-// works in base 2: p = exp2(raw*SC - m*SC) with SC = log2(e)/sqrt(c).
+// Softmax.  Base 2 with a per-query reference r: p = exp2(raw*SC - r), where
+// raw = q.k + sqrt(c)*b and SC = log2(e)/sqrt(c).  The reference is the exact
+// running maximum only when needed: it is set from the first tile with a
+// valid key and moved (rescaling the accumulators) only when a tile's
+// probabilities would exceed 2^12, which the tile sum detects.  Because the
+// final normalisation divides by the sum taken against the same reference,
+// the result is the softmax for any reference; keeping it stale just avoids a
+// max reduction and a rescale per tile.  The row sum is taken from the bf16
+// probabilities that feed the P.V MFMA (v_dot2_f32_bf16 against ones).
 //
 // The N^2 x N logit tensor never leaves the chip (MegaFold explainer,
-// EvoFlash-3D paragraph: the cubic map is produced tile by tile in fast
-// temporary memory and discarded).
+// EvoFlash-3D paragraph: the cubic interaction map is produced tile by tile in
+// fast on-chip memory and discarded).
 #include "common.hpp"
 
 namespace tri {
 
 template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 8 : 4; }
 
+constexpr float SUM_LIMIT = 4096.0f;  // a lane's tile sum above this moves the reference
+
+// bias prep for the forward: out[h][jt][kt][lane][r] = sqrt(c) * bias(j, k) with
+// j = jt*32 + (lane & 31), k = kt*32 + mrow(lane >> 5, r); zero outside n.
+template <typename T>
+__global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias, float* out) {
+  const int nt = (G.n + TILE - 1) / TILE;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one thread per (h, jt, kt, lane)
+  const long long total = (long long)G.H * nt * nt * 64;
+  if (t >= total) return;
+  const int lane = (int)(t & 63);
+  const long long tile = t >> 6;
+  const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
+  const int j = jt * TILE + (lane & 31), g = lane >> 5;
+  f32x4 v[4];
+#pragma unroll
+  for (int r = 0; r < 16; r++) {
+    const int k = kt * TILE + mrow(g, r);
+    v[r >> 2][r & 3] = (j < G.n && k < G.n)
+                           ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C
+                           : 0.0f;
+  }
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+#pragma unroll
+  for (int q = 0; q < 4; q++) o[q] = v[q];
+}
+
 template <typename T, int R>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs<T> a) {
-  constexpr int KP = TILE + kpad<T>();           // LDS row pitch (elements)
-  constexpr int EPV = 16 / sizeof(T);            // elements per 16-byte vector
-  constexpr int CHUNKS = C / EPV;                // vectors per 32-element row
-  __shared__ __align__(16) T sK[R][TILE][KP];    // [row][key][c]
-  __shared__ __align__(16) T sVT[R][C][KP];      // [row][c][key]
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
+  constexpr int KP = TILE + kpad<T>();            // LDS row pitch (elements)
+  constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte vector
+  constexpr int CHUNKS = C / EPV;                 // vectors per 32-element row
+  constexpr int NLOAD = 2 * R * TILE * CHUNKS;    // 16-byte loads per key tile
+  constexpr int LPT = (NLOAD + 255) / 256;        // per thread
+  __shared__ __align__(16) T sKV[2][2 * R][TILE][KP];  // [buffer][K rows 0..R-1, V rows R..2R-1][key][c]
 
   const Geo& G = a.geo;
   const int n = G.n;
+  const int nt = (n + TILE - 1) / TILE;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const int h = blockIdx.z;
   const int row0 = blockIdx.y * R;
-  const int j0 = (blockIdx.x * 4 + w) * TILE;
-  const int j = j0 + l32;
+  const int jt = blockIdx.x * 4 + w;
+  const int j = jt * TILE + l32;
   const bool jvalid = j < n;
   const long long headq = (long long)h * n * C;
+  const f32x4* biasp = reinterpret_cast<const f32x4*>(a.bias_prep) + ((long long)(h * nt + jt) * nt * 64 + lane) * 4;
 
-  // per-row state
   Op<T> qop[R];
   f32x16 o[R];
-  float m[R], l[R];
+  float mb[R], l[R];
   bool degen[R], rvalid[R];
 #pragma unroll
   for (int rr = 0; rr < R; rr++) {
     const int row = row0 + rr;
     rvalid[rr] = row < G.n_rows;
     o[rr] = zero16();
-    m[rr] = NEG_INF;
+    mb[rr] = NEG_INF;
     l[rr] = 0.0f;
-    degen[rr] = false;
-    if (rvalid[rr]) {
-      degen[rr] = !row_has_valid_key(a.mask, G, row, lane);
-      qop[rr] = jvalid ? load_c_op(a.q + row * G.qkv_row + headq + j * G.qkv_pos, g) : zero_op<T>();
-    } else {
-      qop[rr] = zero_op<T>();
-    }
+    degen[rr] = rvalid[rr] ? !row_has_valid_key(a.mask, G, row, lane) : false;
+    qop[rr] = (rvalid[rr] && jvalid) ? load_c_op(a.q + row * G.qkv_row + headq + j * G.qkv_pos, g) : zero_op<T>();
   }
 
-  const int nkt = (n + TILE - 1) / TILE;
-  for (int kt = 0; kt < nkt; kt++) {
+  V16 pre[LPT];
+  uint32_t mnext[R];
+  f32x16 bnext;
+  auto issue = [&](int kt) {
     const int k0 = kt * TILE;
-    __syncthreads();
-    // stage K (row-major) and V (transposed) of the R rows
-    for (int idx = tid; idx < 2 * R * TILE * CHUNKS; idx += 256) {
-      const int ch = idx % CHUNKS;
-      const int key = (idx / CHUNKS) % TILE;
-      const int rr = (idx / (CHUNKS * TILE)) % R;
-      const int isv = idx / (CHUNKS * TILE * R);
-      const int row = row0 + rr, kk = k0 + key;
-      V16 val = {{0u, 0u, 0u, 0u}};
-      if (row < G.n_rows && kk < n) {
-        const T* src = (isv ? a.v : a.k) + row * G.qkv_row + headq + kk * G.qkv_pos + ch * EPV;
-        val = *reinterpret_cast<const V16*>(src);
-      }
-      if (!isv) {
-        *reinterpret_cast<V16*>(&sK[rr][key][ch * EPV]) = val;
-      } else {
-        const T* e = reinterpret_cast<const T*>(&val);
 #pragma unroll
-        for (int t = 0; t < EPV; t++) sVT[rr][ch * EPV + t][key] = e[t];
+    for (int q = 0; q < LPT; q++) {
+      const int idx = tid + 256 * q;
+      pre[q] = V16{{0u, 0u, 0u, 0u}};
+      if (idx < NLOAD) {
+        const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, rr = (idx / (CHUNKS * TILE)) % R;
+        const int isv = idx / (CHUNKS * TILE * R);
+        const int row = row0 + rr, kk = k0 + key;
+        if (row < G.n_rows && kk < n)
+          pre[q] = *reinterpret_cast<const V16*>((isv ? a.v : a.k) + row * G.qkv_row + headq + kk * G.qkv_pos + ch * EPV);
       }
     }
-    // bias tile for this wave's queries (shared by the R rows), raw scale
-    f32x16 binit;
+    if (jt < nt) {
+      const f32x4* bp = biasp + (long long)kt * 64 * 4;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int kk = k0 + mrow(g, r);
-      binit[r] = (jvalid && kk < n)
-                     ? to_f(a.bias[(long long)h * n * n + j * G.bias_q + kk * G.bias_k]) * SQRT_C
-                     : 0.0f;
+      for (int q = 0; q < 4; q++) {
+        const f32x4 v = bp[q];
+        bnext[4 * q] = v[0]; bnext[4 * q + 1] = v[1]; bnext[4 * q + 2] = v[2]; bnext[4 * q + 3] = v[3];
+      }
+    } else {
+      bnext = zero16();
     }
-    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < R; rr++) mnext[rr] = rvalid[rr] ? key_bits(a.mask, G, row0 + rr, k0, lane) : 0u;
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < LPT; q++) {
+      const int idx = tid + 256 * q;
+      if (idx < NLOAD) {
+        const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, slot = idx / (CHUNKS * TILE);
+        *reinterpret_cast<V16*>(&sKV[buf][slot][key][ch * EPV]) = pre[q];
+      }
+    }
+  };
 
+  issue(0);
+  stash(0);
+  f32x16 bcur = bnext;
+  uint32_t mcur[R];
+#pragma unroll
+  for (int rr = 0; rr < R; rr++) mcur[rr] = mnext[rr];
+  __syncthreads();
+
+  for (int kt = 0; kt < nt; kt++) {
+    const int buf = kt & 1, k0 = kt * TILE;
+    if (kt + 1 < nt) issue(kt + 1);
 #pragma unroll
     for (int rr = 0; rr < R; rr++) {
       if (!rvalid[rr]) continue;
-      const int row = row0 + rr;
-      const uint32_t vb = key_bits(a.mask, G, row, k0, lane);
-      const Op<T> kop = load_c_op(&sK[rr][l32][0], g);
-      f32x16 s = mma32(kop, qop[rr], binit);  // s[r]: key k0+mrow(g,r), query j
+      const Op<T> kop = lds_c_op(&sKV[buf][rr][l32][0], g);
+      f32x16 s = mma32(kop, qop[rr], bcur);  // s[r]: key k0+mrow(g,r), query j (raw units)
       if (degen[rr]) {
 #pragma unroll
         for (int r = 0; r < 16; r++) s[r] = (k0 + mrow(g, r) < n) ? 0.0f : NEG_INF;
-      } else if (vb != 0xffffffffu) {
+      } else if (mcur[rr] != 0xffffffffu) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) s[r] = ((vb >> mrow(g, r)) & 1u) ? s[r] : NEG_INF;
+        for (int r = 0; r < 16; r++) s[r] = ((mcur[rr] >> mrow(g, r)) & 1u) ? s[r] : NEG_INF;
       }
-      float tm = s[0];
+      Op<T> pop;
+      float lt = 0.0f;
+      bool fast = __ballot(mb[rr] == NEG_INF) == 0ull;
+      if (fast) {
+        f32x16 p;
 #pragma unroll
-      for (int r = 1; r < 16; r++) tm = fmaxf(tm, s[r]);
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
-      const float mnew = fmaxf(m[rr], tm);
-      const float msafe = (mnew == NEG_INF) ? 0.0f : mnew;
-      const float alpha = fast_exp2((m[rr] - msafe) * SC);
-      l[rr] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; r++) o[rr][r] *= alpha;
-      const float mb = msafe * SC;
-      float ls = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        s[r] = fast_exp2(__builtin_fmaf(s[r], SC, -mb));
-        ls += s[r];
+        for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], SC, -mb[rr]));
+        pop = acc_op<T>(p);
+        lt = op_sum(pop);
+        fast = __ballot(!(lt <= SUM_LIMIT)) == 0ull;
       }
-      l[rr] += ls;
-      m[rr] = mnew;
-      const Op<T> pop = acc_op<T>(s);
-      const Op<T> vop = load_m_op_contig(&sVT[rr][l32][0], g);
+      if (!fast) {
+        // exact reference: the running max (in log2 units) over this and earlier tiles
+        float tm = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; r++) tm = fmaxf(tm, s[r]);
+        tm = fmaxf(tm, __shfl_xor(tm, 32)) * SC;
+        const float mnew = fmaxf(mb[rr], tm);
+        const float alpha = (mb[rr] == NEG_INF) ? 0.0f : fast_exp2(mb[rr] - mnew);
+        l[rr] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; r++) o[rr][r] *= alpha;
+        mb[rr] = mnew;
+        const float msafe = (mnew == NEG_INF) ? 0.0f : mnew;
+        f32x16 p;
+#pragma unroll
+        for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], SC, -msafe));
+        pop = acc_op<T>(p);
+        lt = op_sum(pop);
+      }
+      l[rr] += lt;
+      const Op<T> vop = lds_tr_op<MAP_M>(&sKV[buf][R + rr][0][0], KP, lane);
       o[rr] = mma32(vop, pop, o[rr]);  // o[r]: channel mrow(g,r), query j
     }
+    if (kt + 1 < nt) {
+      stash(buf ^ 1);
+      bcur = bnext;
+#pragma unroll
+      for (int rr = 0; rr < R; rr++) mcur[rr] = mnext[rr];
+    }
+    __syncthreads();
   }
 
   // epilogue: normalise, save attention and log-sum-exp, apply the gate
@@ -149,32 +214,50 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs<T> a) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; s4++) {
       const int c0 = 4 * g + 8 * s4;
+      float av[4], ov[4];
 #pragma unroll
-      for (int t = 0; t < 4; t++) {
-        const float av = o[rr][4 * s4 + t] * inv;
-        const T at = from_f<T>(av);
-        a.attn[ia + c0 + t] = at;
-        const float gt = to_f(a.gate[ig + c0 + t]);
-        a.out[ig + c0 + t] = from_f<T>(sigmoidf_(gt) * av);
+      for (int t = 0; t < 4; t++) av[t] = o[rr][4 * s4 + t] * inv;
+      if constexpr (sizeof(T) == 2) {
+        const bf16x4 gv = *reinterpret_cast<const bf16x4*>(a.gate + ig + c0);
+#pragma unroll
+        for (int t = 0; t < 4; t++) ov[t] = sigmoidf_((float)gv[t]) * av[t];
+        *reinterpret_cast<bf16x4*>(a.attn + ia + c0) = (bf16x4){(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
+        *reinterpret_cast<bf16x4*>(a.out + ig + c0) = (bf16x4){(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+      } else {
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gate + ig + c0);
+#pragma unroll
+        for (int t = 0; t < 4; t++) ov[t] = sigmoidf_(gv[t]) * av[t];
+        *reinterpret_cast<f32x4*>(a.attn + ia + c0) = (f32x4){av[0], av[1], av[2], av[3]};
+        *reinterpret_cast<f32x4*>(a.out + ig + c0) = (f32x4){ov[0], ov[1], ov[2], ov[3]};
       }
     }
     if (g == 0) {
-      float lse;
-      if (degen[rr]) lse = MASK_LOGIT + logf((float)n);
-      else lse = m[rr] * INV_SQRT_C + logf(lt);
+      const float lse = degen[rr] ? MASK_LOGIT + logf((float)n) : (mb[rr] + __log2f(lt)) * LN2;
       a.lse[((long long)row * G.H + h) * n + j] = lse;
     }
   }
 }
 
+size_t fwd_workspace_bytes(int n, int h) {
+  const size_t nt = (size_t)(n + TILE - 1) / TILE;
+  return (size_t)h * nt * nt * 1024 * sizeof(float);
+}
+
 template <typename T, int R>
 hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
-  dim3 grid((a.geo.n + 127) / 128, (a.geo.n_rows + R - 1) / R, a.geo.H);
+  const Geo& G = a.geo;
+  const int nt = (G.n + TILE - 1) / TILE;
+  const long long prep_threads = (long long)G.H * nt * nt * 64;
+  hipLaunchKernelGGL((fwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
+                     a.bias, a.bias_prep);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((G.n + 127) / 128, (G.n_rows + R - 1) / R, G.H);
   hipLaunchKernelGGL((fwd_kernel<T, R>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
-template hipError_t launch_fwd<bf16, 4>(const FwdArgs<bf16>&, hipStream_t);
-template hipError_t launch_fwd<float, 4>(const FwdArgs<float>&, hipStream_t);
+template hipError_t launch_fwd<bf16, 2>(const FwdArgs<bf16>&, hipStream_t);
+template hipError_t launch_fwd<float, 2>(const FwdArgs<float>&, hipStream_t);
 
 }  // namespace tri
