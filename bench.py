@@ -99,6 +99,8 @@ def main():
     ap.add_argument("--n", type=int, default=768)
     ap.add_argument("--cpu-rows", type=int, default=128, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported on this single-GPU build",
@@ -170,6 +172,15 @@ def main():
             stages["bwd_main"] += hip.ms(e[2], e[3])
             stages["dbias_reduce"] += hip.ms(e[3], e[4])
         return total / steps, {k: v / steps for k, v in stages.items()}
+
+    if args.copy_calibration_mib > 0:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale the HBM byte counts
+        src = torch.ones(args.copy_calibration_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_step, stages = timed(0, args.steps, args.warmup)
     flops = 14.0 * n ** 3 * H * c

@@ -12,8 +12,11 @@ SOURCES = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 DEPS = SOURCES + sorted(glob.glob(os.path.join(PKG, "csrc", "*.hpp"))) + [os.path.join(ROOT, "include", "tri_attn.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions stay off: the kernels are written for scalar fp32 VALU.
+# MFMA accumulators stay in VGPR form: the AGPR form makes the compiler shuttle
+# the backward kernel's dK/dV accumulators with v_accvgpr moves.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include")]
 
 

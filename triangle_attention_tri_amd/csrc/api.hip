@@ -85,18 +85,29 @@ Geo make_geo(int n_rows, int n, int h, int ending) {
   return g;
 }
 
-// Key tiles per wave of the per-row backward kernel (0: use the row-group kernel).
+// Key ranges per row and key tiles per wave of the per-row backward kernel
+// (kpw 0: use the row-group kernel).  bf16 rows are split into ranges of at
+// most eight 32-key tiles, so each of the four waves holds at most two key
+// tiles and two workgroups fit on a CU (measured at n = 768: three ranges of
+// eight tiles 1.87 ms, two ranges of twelve 2.21 ms for the main kernel).
+int pick_nsplit(int dtype, int n) {
+  const int nt = (n + TILE - 1) / TILE;
+  if (dtype != TRI_ATTN_BF16) return 1;
+  return (nt + 7) / 8;
+}
 int pick_kpw(int dtype, int n) {
-  const int nt = (n + TILE - 1) / TILE, kpw = (nt + 3) / 4;
-  const int max_kpw = dtype == TRI_ATTN_BF16 ? 6 : 2;
+  const int nt = (n + TILE - 1) / TILE, ns = pick_nsplit(dtype, n);
+  if (ns < 1) return 0;
+  const int tps = (nt + ns - 1) / ns, kpw = (tps + 3) / 4;
+  const int max_kpw = 2;
   if (kpw > max_kpw) return 0;
   const size_t smem = dtype == TRI_ATTN_BF16 ? tile_smem<bf16>(kpw) : tile_smem<float>(kpw);
   return smem <= LDS_LIMIT ? kpw : 0;
 }
 
 struct WsLayout {
-  size_t dA, Dsum, slabs, bias_prep, tslab, total;
-  int rows, groups, kpw;
+  size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, total;
+  int rows, groups, kpw, nsplit;
 };
 
 WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
@@ -109,9 +120,11 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
   const size_t after_d = align256(L.Dsum + (size_t)n_rows * h * n * sizeof(float));
   if (L.kpw > 0) {
     L.rows = 1;
+    L.nsplit = pick_nsplit(dtype, n);
     L.bias_prep = after_d;
-    L.tslab = align256(L.bias_prep + (size_t)h * nt * nt * 1024 * sizeof(float));
-    L.total = align256(L.tslab + (size_t)n_rows * h * nt * nt * 1024 * es);
+    L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * sizeof(float));
+    L.dq_part = align256(L.tslab + (size_t)n_rows * h * nt * nt * 1024 * es);
+    L.total = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * sizeof(float) : 0));
     return L;
   }
   L.rows = pick_rows(dtype, n);
@@ -158,20 +171,14 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.groups = L.groups;
   a.bias_prep = (float*)(base + L.bias_prep);
   a.tslab = (T*)(base + L.tslab);
+  a.dq_part = (float*)(base + L.dq_part);
+  a.nsplit = L.nsplit;
   hipError_t e;
   if (L.kpw > 0) {
     switch (L.kpw) {
       case 1: e = launch_bwd_tile<T, 1>(a, st, ev); break;
       case 2: e = launch_bwd_tile<T, 2>(a, st, ev); break;
-      default:
-        if constexpr (sizeof(T) == 2) {
-          if (L.kpw == 3) e = launch_bwd_tile<T, 3>(a, st, ev);
-          else if (L.kpw == 4) e = launch_bwd_tile<T, 4>(a, st, ev);
-          else if (L.kpw == 5) e = launch_bwd_tile<T, 5>(a, st, ev);
-          else e = launch_bwd_tile<T, 6>(a, st, ev);
-        } else {
-          return TRI_ATTN_EUNSUPPORTED;
-        }
+      default: return TRI_ATTN_EUNSUPPORTED;
     }
   } else if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
   else if (L.rows == 2) e = launch_bwd_rows<T, 2>(a, st, ev);

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void bwd_main_kernel(BwdArgs<T> a) {
       const int rr = (idx / (CHUNKS * TILE)) % R;
       const int isv = idx / (CHUNKS * TILE * R);
       const int row = row0 + rr, kg = k0 + key;
-      V16 val = {{0u, 0u, 0u, 0u}};
+      V16 val = {0u, 0u, 0u, 0u};
       if (row < G.n_rows && kg < n)
         val = *reinterpret_cast<const V16*>((isv ? a.v : a.k) + row * G.qkv_row + headq + kg * G.qkv_pos + ch * EPV);
       if (isv) {

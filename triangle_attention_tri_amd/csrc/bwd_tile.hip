@@ -1,16 +1,18 @@
-// Backward, one workgroup per (row i, head h) -- the path used up to n = 768.
+// Backward, one workgroup per (row i, head h, key range) -- the path used up to
+// n = 768 (bf16) / 256 (fp32).
 //
-// Each of the four waves owns every fourth 32-key tile of the row (up to six)
-// for the whole row: its V tiles sit in registers and its dK / dV
-// accumulators in accumulation registers, so dK and dV are complete when the
-// row ends and are written once.  K of the whole row sits in LDS (it is read
-// both as the logit operand and, transposed, as the dQ operand).  The query
-// tiles are walked in order; the next tile's Q and dA rows (and its
-// log-sum-exp and D values) are loaded into registers while the current one
-// is computed, then written to the other half of a double-buffered LDS area.
-// For every (query tile, key tile) the logit tile S = Q K^T + b and
-// P = exp(S - lse) are recomputed ONCE and feed all four gradients
-// (TurboPairFormer news item, "Dove si impiega il tempo"):
+// The keys of a row are split into nsplit contiguous ranges of at most eight
+// 32-key tiles, so that each of the four waves owns at most two of them and two
+// workgroups fit on a CU.  A wave
+// keeps the V operands of its tiles and their dK / dV accumulators in
+// registers for the whole row, so dK and dV are complete when the row ends and
+// are written once.  K of the key range sits in LDS (read as the logit operand
+// and, transposed, as the dQ operand).  Query tiles are walked in order; the
+// next tile's Q and dA rows and its log-sum-exp / D values are loaded into
+// registers while the current one is computed, then written to the other half
+// of a double-buffered LDS area.  For every (query tile, key tile) the logit
+// tile S = Q K^T + b and P = exp(S - lse) are recomputed ONCE and feed all
+// four gradients (TurboPairFormer news item, "Dove si impiega il tempo"):
 //     dP - D = dA V^T - D     (D folded into the MFMA accumulator input)
 //     dS     = P (dP - D)
 //     dV^T  += dA^T P,   dK^T += Q^T dS,   dQ += dS K,   dbias partial = dS.
@@ -18,10 +20,16 @@
 // and dK products straight from the accumulator; dA^T and Q^T come from the
 // LDS copies through the gfx950 transposing read, and dS goes through a small
 // per-wave LDS tile to become the row operand of dQ.  dQ of a query tile is
-// the sum of the four waves' partials, added in wave order after one barrier.
+// the sum of the four waves' partials, added in wave order after a barrier;
+// with two key ranges each range writes an fp32 partial and a later kernel
+// adds the two in range order.
 // The pair-bias gradient needs a sum over rows i, which no workgroup owns: each
-// row writes its dS tiles (in the operand precision, T) and a separate kernel
-// sums them over rows in ascending order in fp32.
+// row writes its dS tiles (in the operand precision T, as they enter the dQ
+// and dK products) and a separate kernel sums them over rows in ascending
+// order in fp32.
+// A row whose keys are all masked has uniform weights 1/n and no gradient
+// through its logits: it takes a separate short path (dV = mean of dA over the
+// queries, dQ = dK = 0, zero dS tiles) and never enters the tile loop.
 #include "common.hpp"
 
 namespace tri {
@@ -31,11 +39,11 @@ template <typename T> constexpr int tpad() { return sizeof(T) == 2 ? 8 : 4; }
 template <typename T> struct TileSmem {
   static constexpr int KP = TILE + tpad<T>();
   static constexpr size_t tile = sizeof(T) * TILE * KP;
-  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)4 * kpw * tile; }  // K rows of the row
+  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)4 * kpw * tile; }  // K of the key range
   static constexpr size_t qd_bytes = 2 * 2 * tile;                           // Q, dA tiles x 2 buffers
   static constexpr size_t ld_bytes = 2 * 2 * TILE * sizeof(float);           // lse*log2e, -D x 2 buffers
-  static constexpr size_t dt_bytes = 4 * tile;                               // per-wave dS^T tile
-  static constexpr size_t dq_bytes = 2 * 4 * 16 * 64 * sizeof(float);        // dQ partials x 2 buffers
+  static constexpr size_t dt_bytes = 4 * 2 * tile;                           // per-wave dS^T tiles (up to 2)
+  static constexpr size_t dq_bytes = 4 * 16 * 64 * sizeof(float);            // per-wave dQ partials
   static constexpr __host__ __device__ size_t total(int kpw) { return k_bytes(kpw) + qd_bytes + ld_bytes + dt_bytes + dq_bytes; }
 };
 
@@ -89,7 +97,13 @@ __global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias
   const int nt = (G.n + TILE - 1) / TILE;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)G.H * nt * nt * 64;
-  if (t >= total) return;
+  if (t >= total + 64) return;
+  if (t >= total) {  // the zero tile used by rows whose keys are all masked
+    f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+#pragma unroll
+    for (int q = 0; q < 4; q++) o[q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+    return;
+  }
   const int lane = (int)(t & 63);
   const long long tile = t >> 6;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
@@ -162,7 +176,7 @@ __device__ __forceinline__ void wave_sync_lds() {
 }
 
 template <typename T, int KPW>
-__global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel(BwdArgs<T> a) {
   using SM = TileSmem<T>;
   constexpr int KP = SM::KP;
   constexpr int EPV = 16 / sizeof(T), CHUNKS = C / EPV;
@@ -178,20 +192,44 @@ __global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int row = blockIdx.x, h = blockIdx.y;
+  const int row = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  const int tps = (nt + a.nsplit - 1) / a.nsplit;          // key tiles per range
+  const int kt0 = split * tps;                             // first key tile of this range
+  const int nkt = min(tps, nt - kt0);                      // key tiles in this range
   const long long headq = (long long)h * n * C;
   const long long irow = ((long long)row * G.H + h) * n;
   const T* qrow = a.q + row * G.qkv_row + headq;
-  const bool degen = !row_has_valid_key(a.mask, G, row, lane);
-  const float inv_n = fast_exp2(-__log2f((float)n));
-  T* wdt = sDT + w * TILE * KP;
+  T* slab_row = a.tslab + ((long long)row * G.H + h) * nt * nt * 1024 + lane * 16;
+  if (!row_has_valid_key(a.mask, G, row, lane)) {
+    // every key masked: P = 1/n everywhere, dS = 0
+    for (int ktl = w; ktl < nkt; ktl += 4) {
+      for (int jt = 0; jt < nt; jt++) store_tile_op<T>(slab_row + (jt * nt + kt0 + ktl) * 1024, zero_op<T>());
+      const int kk = (kt0 + ktl) * TILE + l32;
+      if (kk >= n) continue;
+      const long long off = row * G.qkv_row + headq + kk * G.qkv_pos;
+      for (int c = 16 * g; c < 16 * g + 16; c++) {
+        float sum = 0.0f;
+        for (int jj = 0; jj < n; jj++) sum += to_f(a.dA[(irow + jj) * C + c]);
+        a.dv[off + c] = from_f<T>(sum / (float)n);
+        a.dk[off + c] = from_f<T>(0.0f);
+      }
+    }
+    for (int e = tid; e < n * C; e += 256) {
+      const int jj = e / C, c = e % C;
+      if (a.nsplit > 1) a.dq_part[((long long)split * G.n_rows * G.H * n + irow + jj) * C + c] = 0.0f;
+      else a.dq[row * G.qkv_row + headq + jj * G.qkv_pos + c] = from_f<T>(0.0f);
+    }
+    return;
+  }
+  T* wdt = sDT + w * 2 * TILE * KP;   // this wave's dS^T tiles, one per key tile it owns
 
-  // K of the whole row into LDS (row-major, key tiles back to back)
-  for (int idx = tid; idx < nt * TILE * CHUNKS; idx += 256) {
-    const int key = idx / CHUNKS, ch = idx % CHUNKS;
-    V16 val = {{0u, 0u, 0u, 0u}};
-    if (key < n) val = *reinterpret_cast<const V16*>(a.k + row * G.qkv_row + headq + key * G.qkv_pos + ch * EPV);
-    *reinterpret_cast<V16*>(sK + key * KP + ch * EPV) = val;
+  // K of the key range into LDS (row-major, key tiles back to back)
+  for (int idx = tid; idx < 4 * KPW * TILE * CHUNKS; idx += 256) {   // tiles past the range stay zero
+    const int kl = idx / CHUNKS, ch = idx % CHUNKS, key = kt0 * TILE + kl;
+    V16 val = {0u, 0u, 0u, 0u};
+    if (kl < nkt * TILE && key < n)
+      val = *reinterpret_cast<const V16*>(a.k + row * G.qkv_row + headq + key * G.qkv_pos + ch * EPV);
+    *reinterpret_cast<V16*>(sK + kl * KP + ch * EPV) = val;
   }
   // this wave's V tiles (B operand of dA V^T, lane = key) and key masks
   Op<T> vb[KPW];
@@ -199,54 +237,67 @@ __global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
   f32x16 dkt[KPW], dvt[KPW];
 #pragma unroll
   for (int t = 0; t < KPW; t++) {
-    const int kk = (t * 4 + w) * TILE + l32;
-    vb[t] = kk < n ? load_c_op(a.v + row * G.qkv_row + headq + kk * G.qkv_pos, g) : zero_op<T>();
-    kbits[t] = key_bits(a.mask, G, row, (t * 4 + w) * TILE, lane);
+    const int ktg = kt0 + t * 4 + w;
+    const int kk = ktg * TILE + l32;
+    vb[t] = (t * 4 + w < nkt && kk < n) ? load_c_op(a.v + row * G.qkv_row + headq + kk * G.qkv_pos, g)
+                                        : zero_op<T>();
+    kbits[t] = (t * 4 + w < nkt) ? key_bits(a.mask, G, row, ktg * TILE, lane) : 0u;  // 0: tile past the range
     dkt[t] = zero16();
     dvt[t] = zero16();
   }
 
-  // query-tile staging
-  V16 qpre[QLPT];
-  f32x4 ldpre = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto issue_q = [&](int jt) {
+  // Query-tile staging.  Each thread moves one 16-byte piece of the Q or dA
+  // tile (two for fp32) and threads 0..15 also four log-sum-exp / D values.
+  // The loads are unconditional (row indices clamped into range) and are
+  // consumed only by the LDS writes after the tile's compute, so they stay in
+  // flight during it.
+  static_assert(QLOADS == 256 * QLPT, "staging assumes whole 16-byte pieces per thread");
+  const int q_which = tid / (TILE * CHUNKS), q_jr = (tid / CHUNKS) % TILE, q_ch = tid % CHUNKS;
+  const int l_which = (tid >> 3) & 1, l_j = 4 * (tid & 7);
+  const float* l_src = l_which ? a.Dsum : a.lse;
+  V16 qpre0, qpre1;
+  f32x4 ldpre;
+  auto q_src = [&](int which, int jj) __attribute__((always_inline)) -> const V16* {
+    return reinterpret_cast<const V16*>(which ? a.dA + (irow + jj) * C : qrow + jj * G.qkv_pos);
+  };
+  auto issue_q = [&](int jt) __attribute__((always_inline)) {
+    if constexpr (QLPT == 1) {
+      qpre0 = q_src(q_which, min(jt * TILE + q_jr, n - 1))[q_ch];
+    } else {
+      // fp32: piece tid covers Q, piece tid + 256 covers dA
+      qpre0 = q_src(0, min(jt * TILE + (tid / CHUNKS), n - 1))[q_ch];
+      qpre1 = q_src(1, min(jt * TILE + (tid / CHUNKS), n - 1))[q_ch];
+    }
 #pragma unroll
-    for (int q = 0; q < QLPT; q++) {
-      const int idx = tid + 256 * q;
-      qpre[q] = V16{{0u, 0u, 0u, 0u}};
-      if (idx < QLOADS) {
-        const int which = idx / (TILE * CHUNKS), jr = (idx / CHUNKS) % TILE, ch = idx % CHUNKS;
-        const int jj = jt * TILE + jr;
-        if (jj < n)
-          qpre[q] = *reinterpret_cast<const V16*>(which ? a.dA + (irow + jj) * C + ch * EPV
-                                                        : qrow + jj * G.qkv_pos + ch * EPV);
-      }
+    for (int t = 0; t < 4; t++) ldpre[t] = l_src[irow + min(jt * TILE + l_j + t, n - 1)];
+  };
+  auto stash_q = [&](int buf, int jt) __attribute__((always_inline)) {
+    if constexpr (QLPT == 1) {
+      *reinterpret_cast<V16*>(sQ + ((buf * 2 + q_which) * TILE + q_jr) * KP + q_ch * EPV) = qpre0;
+    } else {
+      *reinterpret_cast<V16*>(sQ + ((buf * 2 + 0) * TILE + tid / CHUNKS) * KP + q_ch * EPV) = qpre0;
+      *reinterpret_cast<V16*>(sQ + ((buf * 2 + 1) * TILE + tid / CHUNKS) * KP + q_ch * EPV) = qpre1;
     }
     if (tid < 16) {
-      const int which = tid >> 3, j0 = jt * TILE + 4 * (tid & 7);
+      // log2-scaled lse (+inf past n, so those queries get P = 0) and -D
+      const int j0 = jt * TILE + l_j;
+      f32x4 v;
 #pragma unroll
-      for (int t = 0; t < 4; t++) {
-        const int jj = j0 + t;
-        ldpre[t] = which == 0 ? (jj < n ? a.lse[irow + jj] * LOG2E : POS_INF) : (jj < n ? -a.Dsum[irow + jj] : 0.0f);
-      }
+      for (int t = 0; t < 4; t++) v[t] = l_which == 0 ? (j0 + t < n ? ldpre[t] * LOG2E : POS_INF) : -ldpre[t];
+      *reinterpret_cast<f32x4*>(sLD + (buf * 2 + l_which) * TILE + l_j) = v;
     }
-  };
-  auto stash_q = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < QLPT; q++) {
-      const int idx = tid + 256 * q;
-      if (idx < QLOADS) {
-        const int which = idx / (TILE * CHUNKS), jr = (idx / CHUNKS) % TILE, ch = idx % CHUNKS;
-        *reinterpret_cast<V16*>(sQ + ((buf * 2 + which) * TILE + jr) * KP + ch * EPV) = qpre[q];
-      }
-    }
-    if (tid < 16) *reinterpret_cast<f32x4*>(sLD + (buf * 2 + (tid >> 3)) * TILE + 4 * (tid & 7)) = ldpre;
   };
 
-  const float* bp_row = a.bias_prep + (long long)h * nt * nt * 1024 + lane * 16;
+  // bias tiles [h][jt][kt] of the prep buffer; tiles past the key range read the zero tile
+  const float* bias_h = a.bias_prep + (long long)h * nt * nt * 1024 + lane * 16;
+  const float* bias_zero = a.bias_prep + (long long)G.H * nt * nt * 1024 + lane * 16;
+  auto bias_ptr = [&](int jt, int ktl) __attribute__((always_inline)) {
+    return (jt < nt && ktl < nkt) ? bias_h + ((long long)jt * nt + kt0 + ktl) * 1024 : bias_zero;
+  };
+
   issue_q(0);
-  stash_q(0);
-  f32x16 bnext = (w < nt) ? load_tile16<T>(bp_row + (long long)w * 1024) : zero16();
+  stash_q(0, 0);
+  f32x16 bnext = load_tile16<T>(bias_ptr(0, w));
   __syncthreads();
 
   for (int jt = 0; jt < nt; jt++) {
@@ -254,99 +305,100 @@ __global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
     if (jt + 1 < nt) issue_q(jt + 1);
     const T* tq = sQ + (b * 2 + 0) * TILE * KP;
     const T* tda = sQ + (b * 2 + 1) * TILE * KP;
+    const float* tl = sLD + (b * 2 + 0) * TILE + 4 * g;
+    const float* td = sLD + (b * 2 + 1) * TILE + 4 * g;
     const Op<T> qa = lds_c_op(tq + l32 * KP, g);
     const Op<T> daa = lds_c_op(tda + l32 * KP, g);
-    float lse2[16];
-    f32x16 dng;
-#pragma unroll
-    for (int s4 = 0; s4 < 4; s4++) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(sLD + (b * 2 + 0) * TILE + 8 * s4 + 4 * g);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sLD + (b * 2 + 1) * TILE + 8 * s4 + 4 * g);
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-        lse2[4 * s4 + t] = l4[t];
-        dng[4 * s4 + t] = d4[t];
-      }
-    }
-    f32x16 dq = zero16();
-    const float* bp_jt = bp_row + (long long)jt * nt * 1024;
+    const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
+    const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
+    // phase 1: per key tile, recompute S and P once; dV, dK, the dS^T LDS tile, the dbias tile
+    // A tile past the range (ragged n) runs with key mask 0 (P = dS = 0) and
+    // zero K rows, and skips its dS store: the loop has a fixed trip count.
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
-      const int kt = t * 4 + w;
-      if (kt >= nt) break;
-      const f32x16 bcur = bnext;
-      if (kt + 4 < nt) bnext = load_tile16<T>(bp_jt + (long long)(kt + 4) * 1024);
-      else if (jt + 1 < nt && w < nt) bnext = load_tile16<T>(bp_jt + (long long)nt * 1024 + (long long)w * 1024);
-      const T* tk = sK + kt * TILE * KP;
+      const int ktl = t * 4 + w;                 // key tile within the range
+      const int ktg = kt0 + ktl;
+      const f32x16 bias = bnext;                 // prefetched one tile ahead
+      bnext = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, w));
+      const T* tk = sK + ktl * TILE * KP;
       const Op<T> kb = lds_c_op(tk + l32 * KP, g);
-      const f32x16 s = mma32(qa, kb, bcur);        // [query j0+mrow(g,r)][key kt*32+l32], raw units
-      f32x16 p, ds;
-      if (degen) {
-        const bool kin = kt * TILE + l32 < n;
+      const f32x16 s = mma32(qa, kb, bias);      // [query jt*32+mrow(g,r)][key ktg*32+l32], raw units
+      f32x16 p;
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          p[r] = (kin && lse2[r] != POS_INF) ? inv_n : 0.0f;
-          ds[r] = 0.0f;
-        }
-      } else {
+      for (int s4 = 0; s4 < 4; s4++) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(tl + 8 * s4);
 #pragma unroll
-        for (int r = 0; r < 16; r++) p[r] = fast_exp2(__builtin_fmaf(s[r], SC, -lse2[r]));
-        if (kbits[t] != 0xffffffffu) {
-          const bool kv = (kbits[t] >> l32) & 1u;
-#pragma unroll
-          for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
-        }
+        for (int q = 0; q < 4; q++) p[4 * s4 + q] = fast_exp2(__builtin_fmaf(s[4 * s4 + q], SC, -l4[q]));
       }
-      const f32x16 dp = mma32(daa, vb[t], dng);    // dP - D
-      if (!degen) {
+      if (kbits[t] != 0xffffffffu) {
+        const bool kv = (kbits[t] >> l32) & 1u;
 #pragma unroll
-        for (int r = 0; r < 16; r++) ds[r] = p[r] * dp[r];
+        for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
       }
+      f32x16 dng;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + 8 * s4);
+#pragma unroll
+        for (int q = 0; q < 4; q++) dng[4 * s4 + q] = d4[q];
+      }
+      const f32x16 dp = mma32(daa, vb[t], dng);  // dP - D
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; r++) ds[r] = p[r] * dp[r];
       const Op<T> pb = acc_op<T>(p);
       const Op<T> dsb = acc_op<T>(ds);
-      const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
-      dvt[t] = mma32(dat, pb, dvt[t]);             // [channel][key]
-      const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
-      dkt[t] = mma32(qt, dsb, dkt[t]);             // [channel][key]
-      store_dst<T>(wdt, dsb, l32, g);
-      wave_sync_lds();
-      const Op<T> dsa = lds_tr_op<MAP_C>(wdt, KP, lane);   // row = query, contraction = key
-      const Op<T> ktb = lds_tr_op<MAP_C>(tk, KP, lane);    // column = channel, contraction = key
-      dq = mma32(dsa, ktb, dq);                    // [query][channel]
-      store_tile_op<T>(a.tslab + ((((long long)row * G.H + h) * nt + jt) * nt + kt) * 1024 + lane * 16, dsb);
-      wave_sync_lds();
+      dvt[t] = mma32(dat, pb, dvt[t]);           // [channel][key]
+      dkt[t] = mma32(qt, dsb, dkt[t]);           // [channel][key]
+      store_dst<T>(wdt + t * TILE * KP, dsb, l32, g);
+      if (ktl < nkt) store_tile_op<T>(slab_row + (jt * nt + ktg) * 1024, dsb);
     }
-    float* slot = sDQ + (b * 4 + w) * 16 * 64 + lane;
+    wave_sync_lds();
+    // phase 2: dQ += dS K over the wave's key tiles
+    f32x16 dq = zero16();
+#pragma unroll
+    for (int t = 0; t < KPW; t++) {
+      const int ktl = t * 4 + w;
+      const Op<T> dsa = lds_tr_op<MAP_C>(wdt + t * TILE * KP, KP, lane);   // row = query, contraction = key
+      const Op<T> ktb = lds_tr_op<MAP_C>(sK + ktl * TILE * KP, KP, lane);  // column = channel, contraction = key
+      dq = mma32(dsa, ktb, dq);                  // [query][channel]
+    }
+    float* slot = sDQ + w * 16 * 64 + lane;
 #pragma unroll
     for (int r = 0; r < 16; r++) slot[r * 64] = dq[r];
-    if (jt + 1 < nt) stash_q(b ^ 1);
+    if (jt + 1 < nt) stash_q(b ^ 1, jt + 1);
     __syncthreads();
     {
       const int r = tid >> 4, l0 = 4 * (tid & 15);
-      f32x4 sum = *reinterpret_cast<const f32x4*>(sDQ + ((b * 4 + 0) * 16 + r) * 64 + l0);
+      f32x4 sum = *reinterpret_cast<const f32x4*>(sDQ + (0 * 16 + r) * 64 + l0);
 #pragma unroll
       for (int ww = 1; ww < 4; ww++) {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(sDQ + ((b * 4 + ww) * 16 + r) * 64 + l0);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sDQ + (ww * 16 + r) * 64 + l0);
         sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
       }
       const int jj = jt * TILE + mrow(l0 >> 5, r), c0 = l0 & 31;
       if (jj < n) {
-        T* dst = a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0;
-        if constexpr (sizeof(T) == 2)
-          *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(sum[0] * INV_SQRT_C), (bf16)(sum[1] * INV_SQRT_C),
-                                                     (bf16)(sum[2] * INV_SQRT_C), (bf16)(sum[3] * INV_SQRT_C)};
-        else
-          *reinterpret_cast<f32x4*>(dst) = (f32x4){sum[0] * INV_SQRT_C, sum[1] * INV_SQRT_C, sum[2] * INV_SQRT_C,
-                                                   sum[3] * INV_SQRT_C};
+        if (a.nsplit > 1) {
+          *reinterpret_cast<f32x4*>(a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0) = sum;
+        } else {
+          T* dst = a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0;
+          if constexpr (sizeof(T) == 2)
+            *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(sum[0] * INV_SQRT_C), (bf16)(sum[1] * INV_SQRT_C),
+                                                       (bf16)(sum[2] * INV_SQRT_C), (bf16)(sum[3] * INV_SQRT_C)};
+          else
+            *reinterpret_cast<f32x4*>(dst) = (f32x4){sum[0] * INV_SQRT_C, sum[1] * INV_SQRT_C, sum[2] * INV_SQRT_C,
+                                                     sum[3] * INV_SQRT_C};
+        }
       }
     }
+    __syncthreads();
   }
 
   // dK and dV of this wave's key tiles
 #pragma unroll
   for (int t = 0; t < KPW; t++) {
-    const int kk = (t * 4 + w) * TILE + l32;
-    if (kk >= n) continue;
+    const int kk = (kt0 + t * 4 + w) * TILE + l32;
+    if (t * 4 + w >= nkt || kk >= n) continue;
     const long long off = row * G.qkv_row + headq + kk * G.qkv_pos;
 #pragma unroll
     for (int s4 = 0; s4 < 4; s4++) {
@@ -366,6 +418,31 @@ __global__ __launch_bounds__(256, 1) void bwd_tile_kernel(BwdArgs<T> a) {
       }
     }
   }
+}
+
+// dQ = (partial of key range 0 + partial of key range 1 + ...) / sqrt(c), ranges in order.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
+  const Geo& G = a.geo;
+  const long long per_split = (long long)G.n_rows * G.H * G.n * C;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t * 4 >= per_split) return;
+  const long long e = t * 4;
+  f32x4 s = *reinterpret_cast<const f32x4*>(a.dq_part + e);
+  for (int sp = 1; sp < a.nsplit; sp++) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_part + sp * per_split + e);
+    s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
+  }
+  const int c0 = (int)(e % C);
+  const int jj = (int)((e / C) % G.n);
+  const int h = (int)((e / ((long long)C * G.n)) % G.H);
+  const int row = (int)(e / ((long long)C * G.n * G.H));
+  T* dst = a.dq + row * G.qkv_row + (long long)h * G.n * C + jj * G.qkv_pos + c0;
+  if constexpr (sizeof(T) == 2)
+    *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(s[0] * INV_SQRT_C), (bf16)(s[1] * INV_SQRT_C),
+                                               (bf16)(s[2] * INV_SQRT_C), (bf16)(s[3] * INV_SQRT_C)};
+  else
+    *reinterpret_cast<f32x4*>(dst) = (f32x4){s[0] * INV_SQRT_C, s[1] * INV_SQRT_C, s[2] * INV_SQRT_C, s[3] * INV_SQRT_C};
 }
 
 // dbias[h][j][k] = sum over rows (ascending) of the per-row dS tiles, fp32.
@@ -428,7 +505,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   const long long pre_threads = (long long)G.n_rows * G.n * G.H * 4;
   hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long prep_threads = (long long)G.H * nt * nt * 64;
+  const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
   hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
                      a.bias, a.bias_prep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -440,22 +517,24 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(G.n_rows, G.H), dim3(256), TileSmem<T>::total(KPW), st, a);
+  hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(G.n_rows, G.H, a.nsplit), dim3(256), TileSmem<T>::total(KPW), st,
+                     a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_threads = (long long)G.H * nt * nt * 256;
   hipLaunchKernelGGL((dbias_tile_reduce_kernel<T>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.nsplit > 1) {
+    const long long sum_threads = (long long)G.n_rows * G.H * G.n * C / 4;
+    hipLaunchKernelGGL((dq_sum_kernel<T>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
 template hipError_t launch_bwd_tile<bf16, 1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<bf16, 2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<bf16, 3>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<bf16, 4>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<bf16, 5>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<bf16, 6>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<float, 1>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<float, 2>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
 template size_t tile_smem<bf16>(int);

@@ -162,8 +162,9 @@ __device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g
   for (int u = 0; u < 16; u++) row[2 * u + g] = o.f[u];
 }
 
-// 16-byte vector copy helpers for staging
-struct alignas(16) V16 { uint32_t w[4]; };
+// 16-byte vector used for staging copies (a native vector type, so it always
+// lives in registers)
+typedef uint32_t V16 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // Operands read from row-major LDS tiles (32 rows, `pitch` elements per row).
@@ -276,8 +277,10 @@ template <typename T> struct BwdArgs {
   float* Dsum;     // workspace [n_rows][H][n], D = sum_c dA * attn
   float* slabs;    // workspace [groups][H][n][n] dbias partial per row group (row-group kernel)
   int groups;
-  float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order
+  float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order, + one zero tile
   T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
+  float* dq_part;    // workspace [nsplit][n_rows][H][n][C] fp32 dQ partial per key split (nsplit > 1)
+  int nsplit;        // key-range splits per row in the tile kernel
 };
 
 // Does row `row` keep at least one of its n keys?

@@ -102,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
 #pragma unroll
     for (int q = 0; q < LPT; q++) {
       const int idx = tid + 256 * q;
-      pre[q] = V16{{0u, 0u, 0u, 0u}};
+      pre[q] = V16{0u, 0u, 0u, 0u};
       if (idx < NLOAD) {
         const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, rr = (idx / (CHUNKS * TILE)) % R;
         const int isv = idx / (CHUNKS * TILE * R);
