@@ -1,0 +1,134 @@
+"""C ABI contract, checked on the CPU (no kernel is launched).
+
+* libtri_attn.so loads and exports every function declared in include/tri_attn.h.
+* Argument validation returns the documented negative status before any HIP
+  call, so these calls are safe without a GPU.
+* Workspace sizes are consistent with the documented bounds.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import triangle_attention_tri_amd as ta
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tri_attn.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_attn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ta.lib_path):
+        from triangle_attention_tri_amd import _build
+        _build.build()
+    return ta.load()
+
+
+def test_header_symbols_exported(lib):
+    names = declared_functions()
+    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_workspace_size"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in tri_attn.h but not exported"
+
+
+def test_status_strings(lib):
+    for st in (OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, 12345):
+        s = lib.tri_attn_status_string(st)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_version_and_limits(lib):
+    assert lib.tri_attn_version() >= 100
+    assert lib.tri_attn_max_n(ta.BF16) >= 768
+    assert lib.tri_attn_max_n(ta.F32) >= 256
+    assert lib.tri_attn_max_n(7) == 0
+
+
+def fake_ptr(offset=0):
+    # aligned, non-null, never dereferenced: validation rejects the call first
+    return ctypes.c_void_p(0x10000 + offset)
+
+
+def call_fwd(lib, n_rows=8, n=8, h=2, c=32, dtype=ta.BF16, ending=0, ptrs=None, ws_bytes=None, ws=None):
+    p = ptrs or [fake_ptr()] * 8
+    if ws_bytes is None:
+        ws_bytes = lib.tri_attn_fwd_workspace_size(n_rows, n, h, 32, dtype)
+    ws = fake_ptr(0x100000) if ws is None else ws
+    return lib.tri_attn_fwd(n_rows, n, h, c, dtype, ending, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], p[7],
+                            ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def call_bwd(lib, n_rows=8, n=8, h=2, c=32, dtype=ta.BF16, ending=0, ptrs=None, ws_bytes=None, ws=None):
+    p = ptrs or [fake_ptr()] * 13
+    if ws_bytes is None:
+        ws_bytes = lib.tri_attn_bwd_workspace_size(n_rows, n, h, 32, dtype)
+    ws = fake_ptr(0x100000) if ws is None else ws
+    return lib.tri_attn_bwd(n_rows, n, h, c, dtype, ending, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], p[7],
+                            p[8], p[9], p[10], p[11], p[12], ws, ctypes.c_size_t(ws_bytes), None)
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_validation_errors(lib, call):
+    assert call(lib, n_rows=0) == EINVAL
+    assert call(lib, n=0) == EINVAL
+    assert call(lib, h=0) == EINVAL
+    assert call(lib, n_rows=9, n=8) == EINVAL          # more rows than the pair axis holds
+    assert call(lib, dtype=5) == EINVAL
+    assert call(lib, ending=2) == EINVAL
+    assert call(lib, c=16) == EUNSUPPORTED
+    assert call(lib, c=64) == EUNSUPPORTED
+    big = lib.tri_attn_max_n(ta.BF16) + 1
+    assert call(lib, n_rows=1, n=big, ws_bytes=1 << 40) == EUNSUPPORTED
+
+
+@pytest.mark.parametrize("call,nptr", [(call_fwd, 8), (call_bwd, 13)])
+def test_null_and_misaligned(lib, call, nptr):
+    for i in range(nptr):
+        ptrs = [fake_ptr()] * nptr
+        ptrs[i] = None
+        assert call(lib, ptrs=ptrs) == EINVAL, f"null pointer {i}"
+        ptrs[i] = fake_ptr(2)
+        assert call(lib, ptrs=ptrs) == EINVAL, f"misaligned pointer {i}"
+
+
+@pytest.mark.parametrize("call", [call_fwd, call_bwd])
+def test_workspace_errors(lib, call):
+    assert call(lib, ws=ctypes.c_void_p(0)) == EWORKSPACE
+    need = (lib.tri_attn_fwd_workspace_size if call is call_fwd else lib.tri_attn_bwd_workspace_size)(8, 8, 2, 32,
+                                                                                                       ta.BF16)
+    assert need > 0
+    assert call(lib, ws_bytes=need - 1) == EWORKSPACE
+    assert call(lib, ws=fake_ptr(0x100000 + 16)) == EINVAL   # workspace must be 256-byte aligned
+
+
+def test_workspace_sizes(lib):
+    for dt in (ta.BF16, ta.F32):
+        assert lib.tri_attn_bwd_workspace_size(8, 8, 2, 16, dt) == 0
+        assert lib.tri_attn_fwd_workspace_size(0, 8, 2, 32, dt) == 0
+        prev = 0
+        for n in (1, 17, 64, 127, 256):
+            b = lib.tri_attn_bwd_workspace_size(n, n, 4, 32, dt)
+            f = lib.tri_attn_fwd_workspace_size(n, n, 4, 32, dt)
+            assert b % 256 == 0 and f % 256 == 0
+            assert b > prev
+            prev = b
+            # at least the gradient reaching the pre-gate attention and the per-query D
+            assert b >= n * 4 * n * 32 * (2 if dt == ta.BF16 else 4) + n * 4 * n * 4
+
+
+def test_binding_rejects_bad_inputs():
+    q = torch.zeros((4, 2, 4, 32), dtype=torch.float16)
+    with pytest.raises(TypeError):
+        ta.fwd(q, q, q, torch.zeros((2, 4, 4), dtype=torch.float16), torch.zeros((4, 4, 2, 32), dtype=torch.float16))

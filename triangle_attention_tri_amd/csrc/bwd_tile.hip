@@ -122,18 +122,6 @@ __global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias
 }
 
 template <typename T>
-__device__ __forceinline__ f32x16 load_tile16(const float* base) {
-  const f32x4* p = reinterpret_cast<const f32x4*>(base);
-  f32x16 v;
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    const f32x4 x = p[q];
-    v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
-  }
-  return v;
-}
-
-template <typename T>
 __device__ __forceinline__ void store_tile_op(T* dst, const Op<T>& o);
 template <>
 __device__ __forceinline__ void store_tile_op<bf16>(bf16* dst, const Op<bf16>& o) {
@@ -192,7 +180,9 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int row = blockIdx.x, h = blockIdx.y, split = blockIdx.z;
+  // work item (key range fastest, then row, then head), XCD-ordered
+  const int item = xcd_item(blockIdx.x, a.nsplit * G.n_rows * G.H);
+  const int split = item % a.nsplit, row = (item / a.nsplit) % G.n_rows, h = item / (a.nsplit * G.n_rows);
   const int tps = (nt + a.nsplit - 1) / a.nsplit;          // key tiles per range
   const int kt0 = split * tps;                             // first key tile of this range
   const int nkt = min(tps, nt - kt0);                      // key tiles in this range
@@ -517,8 +507,8 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(G.n_rows, G.H, a.nsplit), dim3(256), TileSmem<T>::total(KPW), st,
-                     a);
+  hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(a.nsplit * G.n_rows * G.H), dim3(256), TileSmem<T>::total(KPW),
+                     st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_threads = (long long)G.H * nt * nt * 256;

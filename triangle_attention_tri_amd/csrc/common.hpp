@@ -283,6 +283,34 @@ template <typename T> struct BwdArgs {
   int nsplit;        // key-range splits per row in the tile kernel
 };
 
+// 16 consecutive floats (64 bytes, 16-byte aligned) as one accumulator tile's
+// worth of registers.
+template <typename T>
+__device__ __forceinline__ f32x16 load_tile16(const float* base) {
+  const f32x4* p = reinterpret_cast<const f32x4*>(base);
+  f32x16 v;
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    const f32x4 x = p[q];
+    v[4 * q] = x[0]; v[4 * q + 1] = x[1]; v[4 * q + 2] = x[2]; v[4 * q + 3] = x[3];
+  }
+  return v;
+}
+
+// XCD-aware work order.  Workgroups are dispatched to the eight XCDs round
+// robin (workgroup b runs on XCD b % 8, each with its own L2).  This maps the
+// linear workgroup id to a work item so that every XCD receives one contiguous
+// run of items, in order: items that share inputs (the query blocks of one row
+// in the forward, the key ranges of one row in the backward) then run on the
+// same XCD at nearly the same time and share its L2.  A bijection on
+// [0, total) for any total.
+__device__ __forceinline__ int xcd_item(int L, int total) {
+  constexpr int X = 8;
+  const int q = total / X, rem = total % X;
+  const int x = L % X, local = L / X;
+  return x * q + min(x, rem) + local;
+}
+
 // Does row `row` keep at least one of its n keys?
 __device__ __forceinline__ bool row_has_valid_key(const uint8_t* mask, const Geo& g, int row, int lane) {
   if (mask == nullptr) return true;

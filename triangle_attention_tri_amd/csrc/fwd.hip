@@ -58,26 +58,44 @@ __global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias
   for (int q = 0; q < 4; q++) o[q] = v[q];
 }
 
+// Longest key axis whose per-tile mask words fit the LDS table below.
+constexpr int FWD_MAX_TILES = 64;
+
 template <typename T, int R>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
   constexpr int KP = TILE + kpad<T>();            // LDS row pitch (elements)
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte vector
   constexpr int CHUNKS = C / EPV;                 // vectors per 32-element row
   constexpr int NLOAD = 2 * R * TILE * CHUNKS;    // 16-byte loads per key tile
-  constexpr int LPT = (NLOAD + 255) / 256;        // per thread
+  constexpr int LPT = NLOAD / 256;                // per thread
+  static_assert(NLOAD % 256 == 0, "whole 16-byte pieces per thread");
   __shared__ __align__(16) T sKV[2][2 * R][TILE][KP];  // [buffer][K rows 0..R-1, V rows R..2R-1][key][c]
+  __shared__ uint32_t sMask[R][FWD_MAX_TILES];         // kept-key bits of every key tile of the R rows
 
   const Geo& G = a.geo;
   const int n = G.n;
   const int nt = (n + TILE - 1) / TILE;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
-  const int h = blockIdx.z;
-  const int row0 = blockIdx.y * R;
-  const int jt = blockIdx.x * 4 + w;
+  // work item (query block fastest, then row group, then head), XCD-ordered
+  const int nqb = (n + 127) / 128, nrg = (G.n_rows + R - 1) / R;
+  const int item = xcd_item(blockIdx.x, nqb * nrg * G.H);
+  const int qb = item % nqb, h = item / (nqb * nrg);
+  const int row0 = ((item / nqb) % nrg) * R;
+  const int jt = qb * 4 + w;
   const int j = jt * TILE + l32;
   const bool jvalid = j < n;
   const long long headq = (long long)h * n * C;
-  const f32x4* biasp = reinterpret_cast<const f32x4*>(a.bias_prep) + ((long long)(h * nt + jt) * nt * 64 + lane) * 4;
+  // bias tiles of this wave's query tile (a wave past the last query tile reads the last one, unused)
+  const f32x4* biasp = reinterpret_cast<const f32x4*>(a.bias_prep) +
+                       ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 4;
+
+  // key masks: one word per (row, key tile); keys past n are never kept
+  for (int idx = w; idx < R * nt; idx += 4) {
+    const int rr = idx / nt, kt = idx % nt;
+    const int row = min(row0 + rr, G.n_rows - 1);
+    const uint32_t bits = key_bits(a.mask, G, row, kt * TILE, lane);
+    if (lane == 0) sMask[rr][kt] = bits;
+  }
 
   Op<T> qop[R];
   f32x16 o[R];
@@ -94,69 +112,47 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
     qop[rr] = (rvalid[rr] && jvalid) ? load_c_op(a.q + row * G.qkv_row + headq + j * G.qkv_pos, g) : zero_op<T>();
   }
 
+  // K / V staging: every load is unconditional (row and key clamped into range;
+  // keys past n are masked out, rows past n_rows are never computed)
   V16 pre[LPT];
-  uint32_t mnext[R];
-  f32x16 bnext;
-  auto issue = [&](int kt) {
+  auto issue = [&](int kt_in) __attribute__((always_inline)) {
+    const int kt = min(kt_in, nt - 1);
+#pragma unroll
+    for (int q = 0; q < LPT; q++) {
+      const int idx = tid + 256 * q;
+      const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, rr = (idx / (CHUNKS * TILE)) % R;
+      const int isv = idx / (CHUNKS * TILE * R);
+      const int row = min(row0 + rr, G.n_rows - 1), kk = min(kt * TILE + key, n - 1);
+      pre[q] = *reinterpret_cast<const V16*>((isv ? a.v : a.k) + row * G.qkv_row + headq + kk * G.qkv_pos + ch * EPV);
+    }
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LPT; q++) {
+      const int idx = tid + 256 * q;
+      const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, slot = idx / (CHUNKS * TILE);
+      *reinterpret_cast<V16*>(&sKV[buf][slot][key][ch * EPV]) = pre[q];
+    }
+  };
+  auto load_bias = [&](int kt) __attribute__((always_inline)) {
+    return load_tile16<T>(reinterpret_cast<const float*>(biasp + (long long)min(kt, nt - 1) * 64 * 4));
+  };
+
+  // one key tile for all R rows
+  auto tile = [&](int kt, int buf, const f32x16& bias) __attribute__((always_inline)) {
     const int k0 = kt * TILE;
-#pragma unroll
-    for (int q = 0; q < LPT; q++) {
-      const int idx = tid + 256 * q;
-      pre[q] = V16{0u, 0u, 0u, 0u};
-      if (idx < NLOAD) {
-        const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, rr = (idx / (CHUNKS * TILE)) % R;
-        const int isv = idx / (CHUNKS * TILE * R);
-        const int row = row0 + rr, kk = k0 + key;
-        if (row < G.n_rows && kk < n)
-          pre[q] = *reinterpret_cast<const V16*>((isv ? a.v : a.k) + row * G.qkv_row + headq + kk * G.qkv_pos + ch * EPV);
-      }
-    }
-    if (jt < nt) {
-      const f32x4* bp = biasp + (long long)kt * 64 * 4;
-#pragma unroll
-      for (int q = 0; q < 4; q++) {
-        const f32x4 v = bp[q];
-        bnext[4 * q] = v[0]; bnext[4 * q + 1] = v[1]; bnext[4 * q + 2] = v[2]; bnext[4 * q + 3] = v[3];
-      }
-    } else {
-      bnext = zero16();
-    }
-#pragma unroll
-    for (int rr = 0; rr < R; rr++) mnext[rr] = rvalid[rr] ? key_bits(a.mask, G, row0 + rr, k0, lane) : 0u;
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < LPT; q++) {
-      const int idx = tid + 256 * q;
-      if (idx < NLOAD) {
-        const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, slot = idx / (CHUNKS * TILE);
-        *reinterpret_cast<V16*>(&sKV[buf][slot][key][ch * EPV]) = pre[q];
-      }
-    }
-  };
-
-  issue(0);
-  stash(0);
-  f32x16 bcur = bnext;
-  uint32_t mcur[R];
-#pragma unroll
-  for (int rr = 0; rr < R; rr++) mcur[rr] = mnext[rr];
-  __syncthreads();
-
-  for (int kt = 0; kt < nt; kt++) {
-    const int buf = kt & 1, k0 = kt * TILE;
-    if (kt + 1 < nt) issue(kt + 1);
 #pragma unroll
     for (int rr = 0; rr < R; rr++) {
       if (!rvalid[rr]) continue;
+      const uint32_t mbits = sMask[rr][kt];
       const Op<T> kop = lds_c_op(&sKV[buf][rr][l32][0], g);
-      f32x16 s = mma32(kop, qop[rr], bcur);  // s[r]: key k0+mrow(g,r), query j (raw units)
+      f32x16 s = mma32(kop, qop[rr], bias);  // s[r]: key k0+mrow(g,r), query j (raw units)
       if (degen[rr]) {
 #pragma unroll
         for (int r = 0; r < 16; r++) s[r] = (k0 + mrow(g, r) < n) ? 0.0f : NEG_INF;
-      } else if (mcur[rr] != 0xffffffffu) {
+      } else if (mbits != 0xffffffffu) {
 #pragma unroll
-        for (int r = 0; r < 16; r++) s[r] = ((mcur[rr] >> mrow(g, r)) & 1u) ? s[r] : NEG_INF;
+        for (int r = 0; r < 16; r++) s[r] = ((mbits >> mrow(g, r)) & 1u) ? s[r] : NEG_INF;
       }
       Op<T> pop;
       float lt = 0.0f;
@@ -192,12 +188,26 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
       const Op<T> vop = lds_tr_op<MAP_M>(&sKV[buf][R + rr][0][0], KP, lane);
       o[rr] = mma32(vop, pop, o[rr]);  // o[r]: channel mrow(g,r), query j
     }
-    if (kt + 1 < nt) {
-      stash(buf ^ 1);
-      bcur = bnext;
-#pragma unroll
-      for (int rr = 0; rr < R; rr++) mcur[rr] = mnext[rr];
-    }
+  };
+
+  issue(0);
+  stash(0);
+  f32x16 bA = load_bias(0), bB;
+  __syncthreads();
+  // Two key tiles per iteration, so the two bias tiles alternate between fixed
+  // registers; the prefetch is unconditional (a tile index past the end is
+  // clamped and its data never used), so no register copy waits on it.
+  for (int kt = 0; kt < nt; kt += 2) {
+    issue(kt + 1);
+    bB = load_bias(kt + 1);
+    tile(kt, 0, bA);
+    stash(1);
+    __syncthreads();
+    if (kt + 1 >= nt) break;
+    issue(kt + 2);
+    bA = load_bias(kt + 2);
+    tile(kt + 1, 1, bB);
+    stash(0);
     __syncthreads();
   }
 
@@ -252,8 +262,8 @@ hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
                      a.bias, a.bias_prep);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 grid((G.n + 127) / 128, (G.n_rows + R - 1) / R, G.H);
-  hipLaunchKernelGGL((fwd_kernel<T, R>), grid, dim3(256), 0, st, a);
+  const int blocks = ((G.n + 127) / 128) * ((G.n_rows + R - 1) / R) * G.H;
+  hipLaunchKernelGGL((fwd_kernel<T, R>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
