@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--n", type=int, default=768)
-    ap.add_argument("--cpu-rows", type=int, default=128, help="rows of the oracle CPU sample (0 = skip)")
+    ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (counter calibration)")
@@ -192,7 +192,7 @@ def main():
     dom = max(("fwd", "bwd_main"), key=lambda k: stages[k])
     bound, work = algo[dom]
     achieved = work / (stages[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_tile_kernel"}
     roofline = {"kernel": kernel_names[dom], "bound": bound, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(kernel_names[dom]), "launch_ms": round(stages[dom], 4)}
