@@ -48,30 +48,52 @@ template <typename T> struct TileSmem {
 };
 
 // ---------------------------------------------------------------------------
-// gate backward + D, four threads per (row, query, head), eight channels each
+// gate backward + D, four threads per (row, query, head), eight channels each.
+// Grid: x covers (query, head, quarter) of one row, y is the row; every
+// thread moves three 8-channel vectors in and two out with vector accesses.
+template <typename T> __device__ __forceinline__ void load8(const T* p, float (&f)[8]);
+template <> __device__ __forceinline__ void load8<bf16>(const bf16* p, float (&f)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int c = 0; c < 8; c++) f[c] = (float)v[c];
+}
+template <> __device__ __forceinline__ void load8<float>(const float* p, float (&f)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int c = 0; c < 4; c++) { f[c] = a[c]; f[c + 4] = b[c]; }
+}
+template <typename T> __device__ __forceinline__ void store8(T* p, const float (&f)[8]);
+template <> __device__ __forceinline__ void store8<bf16>(bf16* p, const float (&f)[8]) {
+  bf16x8 v;
+#pragma unroll
+  for (int c = 0; c < 8; c++) v[c] = (bf16)f[c];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+template <> __device__ __forceinline__ void store8<float>(float* p, const float (&f)[8]) {
+  *reinterpret_cast<f32x4*>(p) = (f32x4){f[0], f[1], f[2], f[3]};
+  *reinterpret_cast<f32x4*>(p + 4) = (f32x4){f[4], f[5], f[6], f[7]};
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_pre_vec_kernel(BwdArgs<T> a) {
   constexpr int EPT = 8;  // channels per thread
   const Geo& G = a.geo;
-  const long long total = (long long)G.n_rows * G.n * G.H * 4;
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool live = t < total;
-  const long long pr = live ? t >> 2 : 0;
-  const int part = (int)(t & 3);
-  const int h = (int)(pr % G.H);
-  const int j = (int)((pr / G.H) % G.n);
-  const int row = (int)(pr / ((long long)G.H * G.n));
+  const int per_row = G.n * G.H * 4;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  const int row = blockIdx.y;
+  const bool live = t < per_row;
+  const int pr = live ? t >> 2 : 0;
+  const int part = t & 3;
+  const int h = pr % G.H;
+  const int j = pr / G.H;
   const long long ip = row * G.pair_row + j * G.pair_pos + (long long)h * C + part * EPT;
   const long long ia = (((long long)row * G.H + h) * G.n + j) * C + part * EPT;
   float dsum = 0.0f;
   if (live) {
     float gt[EPT], dov[EPT], av[EPT], dg[EPT], da[EPT];
-#pragma unroll
-    for (int c = 0; c < EPT; c++) {
-      gt[c] = to_f(a.gate[ip + c]);
-      dov[c] = to_f(a.dout[ip + c]);
-      av[c] = to_f(a.attn[ia + c]);
-    }
+    load8(a.gate + ip, gt);
+    load8(a.dout + ip, dov);
+    load8(a.attn + ia, av);
 #pragma unroll
     for (int c = 0; c < EPT; c++) {
       const float sg = sigmoidf_(gt[c]);
@@ -79,11 +101,8 @@ __global__ __launch_bounds__(256) void bwd_pre_vec_kernel(BwdArgs<T> a) {
       dg[c] = dov[c] * av[c] * sg * (1.0f - sg);
       dsum += da[c] * av[c];
     }
-#pragma unroll
-    for (int c = 0; c < EPT; c++) {
-      a.dgate[ip + c] = from_f<T>(dg[c]);
-      a.dA[ia + c] = from_f<T>(da[c]);
-    }
+    store8(a.dgate + ip, dg);
+    store8(a.dA + ia, da);
   }
   dsum += __shfl_xor(dsum, 1);
   dsum += __shfl_xor(dsum, 2);
@@ -492,8 +511,9 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   const int nt = (G.n + TILE - 1) / TILE;
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  const long long pre_threads = (long long)G.n_rows * G.n * G.H * 4;
-  hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256)), dim3(256), 0, st, a);
+  const int pre_threads = G.n * G.H * 4;  // per row
+  hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
+                     dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
   hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
