@@ -83,3 +83,31 @@ def random_mask(n: int, seed: int, p_keep: float = 0.7, full_rows: tuple = ()) -
     for r in full_rows:
         m[r, :] = 0
     return m
+
+
+def block_inputs(n: int, cz: int = 128, h: int = 4, c: int = 32, dtype=torch.bfloat16, seed: int = 4,
+                 affine: bool = False) -> dict:
+    """Seeded inputs of the LayerNorm + projections + attention + output-linear block.
+
+    Draw order: z [n,n,cz] ~ N(0,1); w_qkvg [4*h*c, cz], w_bias [h, cz] and
+    w_o [cz, h*c] ~ N(0, 1/cz) (standard deviation 1/sqrt(cz)); dy [n,n,cz] ~ N(0,1).
+    gamma = 1 and beta = 0 unless ``affine`` (then gamma ~ 1 + 0.1 N(0,1) and
+    beta ~ 0.1 N(0,1), drawn last), so that tests can see both LayerNorm
+    parameters act.  bf16 rounds every tensor (the oracle reads the rounded
+    values); gamma and beta are kept in the same dtype.
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    z = torch.randn((n, n, cz), generator=g)
+    w_qkvg = torch.randn((4 * h * c, cz), generator=g) / cz ** 0.5
+    w_bias = torch.randn((h, cz), generator=g) / cz ** 0.5
+    w_o = torch.randn((cz, h * c), generator=g) / (h * c) ** 0.5
+    dy = torch.randn((n, n, cz), generator=g)
+    if affine:
+        gamma = 1.0 + 0.1 * torch.randn(cz, generator=g)
+        beta = 0.1 * torch.randn(cz, generator=g)
+    else:
+        gamma, beta = torch.ones(cz), torch.zeros(cz)
+    out = dict(z=z, w_qkvg=w_qkvg, w_bias=w_bias, w_o=w_o, dy=dy, gamma=gamma, beta=beta)
+    if dtype != torch.float32:
+        out = {key: t.to(dtype) for key, t in out.items()}
+    return out
