@@ -149,6 +149,77 @@ int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending
                           void *workspace, size_t workspace_bytes, tri_attn_stream_t stream,
                           tri_attn_event_t *stage_events);
 
+/* ------------------------------------------------------------------------
+ * The block around the attention: LayerNorm + projection front end and the
+ * output linear, forward and backward.  The pages attribute the rest of the
+ * pair stack's time to these LayerNorm and linear layers (TurboPairFormer news
+ * item, "Dove si impiega il tempo"; ScaleFold summary, fused LayerNorm and
+ * linear kernels) and fuse them into few passes (MegaFold explainer, EvoFusion
+ * paragraph).  Written out, for every pair (a, b):
+ *
+ *   x_n   = (z[a,b,:] - mean) / sqrt(var + eps)     biased variance over c_z
+ *   xhat  = x_n * gamma + beta
+ *   q[a,h,b,:] | k | v | gate[a,b,h,:] = xhat . w_qkvg^T   (four blocks of h*c rows)
+ *   bias[h,a,b] = xhat . w_bias[h,:]
+ *   y[a,b,:] = out[a,b,:,:].flatten() . w_o^T
+ *
+ * The projections act on each pair alone, so the same calls serve the starting
+ * and the ending node: tensors stay in the caller's pair layout and only the
+ * attention call's `ending` flag differs.
+ *
+ * Compiled for dtype TRI_ATTN_BF16 with c_z = 128, c = 32, h*c = 128 only
+ * (TRI_ATTN_EUNSUPPORTED otherwise); statistics are fp32, accumulation fp32.
+ * Weights use the (out, in) convention of a linear layer: w_qkvg [4*h*c][c_z]
+ * (rows: q as h*c + channel, then k, v, gate), w_bias [h][c_z], w_o [c_z][h*c].
+ * Rows: a call processes pair rows a = 0..n_rows-1 of z [n_rows][n][c_z]; the
+ * outputs q, k, v [n_rows][h][n][c], gate [n_rows][n][h][c] and the statistics
+ * [n_rows][n] start at that slice; bias / dbias are addressed as
+ * ptr[hh*n*n + a*n + b] (pass the full tensor's address + a0*n for a slice).
+ * Alignment: 16 bytes for every tensor except bias, dbias, the weight and
+ * LayerNorm gradients (2 bytes) and the statistics (4 bytes).
+ * ------------------------------------------------------------------------ */
+
+/* Front end forward: writes q, k, v, gate, bias and the LayerNorm statistics
+ * ln_mean, ln_rstd (fp32, kept for the backward).  0 < ln_eps < 1. */
+int tri_attn_ln_proj_fwd(int n_rows, int n, int cz, int h, int c, int dtype,
+                         const void *z, const void *ln_gamma, const void *ln_beta, float ln_eps,
+                         const void *w_qkvg, const void *w_bias,
+                         void *q, void *k, void *v, void *gate, void *bias,
+                         float *ln_mean, float *ln_rstd, tri_attn_stream_t stream);
+
+/* Bytes of device workspace tri_attn_ln_proj_bwd needs (0 on bad args). */
+size_t tri_attn_ln_proj_bwd_workspace_size(int n_rows, int n, int cz, int h, int c, int dtype);
+
+/* Front end backward.  Inputs: z, gamma, beta, the saved statistics, the
+ * weights and the gradients of the five projected tensors (dbias is the
+ * complete gradient of bias, e.g. the attention backward's dbias).  Outputs
+ * (overwritten): dz [n_rows][n][c_z]; dgamma, dbeta [c_z]; dw_qkvg, dw_bias,
+ * each summed over this call's pairs in a fixed order (bitwise identical across
+ * calls).  workspace: 256-byte aligned, contents on entry ignored. */
+int tri_attn_ln_proj_bwd(int n_rows, int n, int cz, int h, int c, int dtype,
+                         const void *z, const void *ln_gamma, const void *ln_beta,
+                         const float *ln_mean, const float *ln_rstd,
+                         const void *w_qkvg, const void *w_bias,
+                         const void *dq, const void *dk, const void *dv, const void *dgate,
+                         const void *dbias,
+                         void *dz, void *dgamma, void *dbeta, void *dw_qkvg, void *dw_bias,
+                         void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
+
+/* Output linear forward: y [n_pairs][c_out] = x [n_pairs][c_in] . w^T, w [c_out][c_in]
+ * (x is the attention output viewed as [pairs][h*c]).  c_in = c_out = 128. */
+int tri_attn_out_proj_fwd(int n_pairs, int c_in, int c_out, int dtype,
+                          const void *x, const void *w, void *y, tri_attn_stream_t stream);
+
+/* Bytes of device workspace tri_attn_out_proj_bwd needs (0 on bad args). */
+size_t tri_attn_out_proj_bwd_workspace_size(int n_pairs, int c_in, int c_out, int dtype);
+
+/* Output linear backward: dx = dy . w; dw = dy^T . x summed over pairs in a
+ * fixed order.  Outputs overwritten; workspace as above. */
+int tri_attn_out_proj_bwd(int n_pairs, int c_in, int c_out, int dtype,
+                          const void *x, const void *w, const void *dy,
+                          void *dx, void *dw, void *workspace, size_t workspace_bytes,
+                          tri_attn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

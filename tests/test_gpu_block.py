@@ -1,0 +1,138 @@
+"""GPU parity of the block around the attention: LayerNorm + projection front end
+and the output linear, forward and backward, through the C ABI, against the
+fp64 oracle (oracle/block.py).  Bar: normwise 2e-2 (bf16 inputs/outputs, fp32
+accumulation); the LayerNorm statistics (fp32 outputs) 1e-5.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block as B
+import triangle_attention_tri_amd as ta
+from triangle_attention_tri_amd import inputs
+from tests.helpers import assert_close
+
+pytestmark = pytest.mark.gpu
+H, C, CZ = 4, 32, 128
+TOL = 2e-2
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(x, device):
+    return {k: v.to(device) for k, v in x.items()}
+
+
+def check_front_fwd(n, seed, device, affine=True):
+    x = inputs.block_inputs(n, seed=seed, affine=affine)
+    xd = dev(x, device)
+    q, k, v, gate, bias, mean, rstd = ta.ln_proj_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"])
+    torch.cuda.synchronize()
+    ref = B.ln_proj_fwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], H, C)
+    for name, got in dict(q=q, k=k, v=v, gate=gate, bias=bias).items():
+        assert_close(f"n{n}:{name}", got.cpu(), ref[name], TOL)
+    assert_close(f"n{n}:mean", mean.cpu(), ref["mean"], 1e-5)
+    assert_close(f"n{n}:rstd", rstd.cpu(), ref["rstd"], 1e-5)
+    return x, xd, (q, k, v, gate, bias, mean, rstd)
+
+
+@pytest.mark.parametrize("n", [1, 5, 37, 64])
+def test_ln_proj_fwd(device, n):
+    log(f"ln_proj_fwd n={n}")
+    check_front_fwd(n, seed=10 + n, device=device)
+
+
+@pytest.mark.parametrize("n", [1, 5, 37, 64])
+def test_ln_proj_bwd(device, n):
+    log(f"ln_proj_bwd n={n}")
+    x = inputs.block_inputs(n, seed=20 + n, affine=True)
+    gr = inputs.proj_grad_inputs(n, seed=30 + n)
+    xd, gd = dev(x, device), dev(gr, device)
+    _, _, _, _, _, mean, rstd = ta.ln_proj_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"])
+    got = ta.ln_proj_bwd(xd["z"], xd["gamma"], xd["beta"], mean, rstd, xd["w_qkvg"], xd["w_bias"], gd["dq"], gd["dk"],
+                         gd["dv"], gd["dgate"], gd["dbias"])
+    torch.cuda.synchronize()
+    ref = B.ln_proj_bwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], gr["dq"], gr["dk"], gr["dv"],
+                        gr["dgate"], gr["dbias"], H, C)
+    errs = {}
+    for name, t in zip(("dz", "dgamma", "dbeta", "dw_qkvg", "dw_bias"), got):
+        errs[name] = assert_close(f"n{n}:{name}", t.cpu(), ref[name], TOL)
+    log(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.parametrize("n", [1, 7, 40])
+def test_out_proj(device, n):
+    log(f"out_proj n={n}")
+    g = torch.Generator().manual_seed(40 + n)
+    o = torch.randn((n, n, H, C), generator=g).bfloat16()
+    w_o = (torch.randn((CZ, H * C), generator=g) / 128 ** 0.5).bfloat16()
+    dy = torch.randn((n, n, CZ), generator=g).bfloat16()
+    od, wd, dyd = o.to(device), w_o.to(device), dy.to(device)
+    y = ta.out_proj_fwd(od, wd)
+    d_o, dw_o = ta.out_proj_bwd(od, wd, dyd)
+    torch.cuda.synchronize()
+    assert_close("y", y.cpu(), B.out_proj_fwd(o, w_o), TOL)
+    ref = B.out_proj_bwd(o, w_o, dy)
+    assert_close("do", d_o.cpu(), ref["do"], TOL)
+    assert_close("dw_o", dw_o.cpu(), ref["dw_o"], TOL)
+
+
+@pytest.mark.parametrize("ending", [False, True])
+def test_block_small(device, ending):
+    """The whole block (front end -> attention -> output linear), forward and backward."""
+    n = 48
+    log(f"block n={n} ending={ending}")
+    x = inputs.block_inputs(n, seed=50, affine=True)
+    xd = dev(x, device)
+    y, saved = ta.block_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"], ending=ending)
+    grads = ta.block_bwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"], saved, xd["dy"],
+                         ending=ending)
+    torch.cuda.synchronize()
+    ref = B.block_bwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], x["w_o"], x["dy"], H, C, ending=ending)
+    errs = {"y": assert_close("y", y.cpu(), ref["y"], TOL)}
+    for name in ("dz", "dgamma", "dbeta", "dw_qkvg", "dw_bias", "dw_o"):
+        errs[name] = assert_close(name, grads[name].cpu(), ref[name], TOL)
+    log(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+def test_front_end_n768(device):
+    """Front end forward and backward at the block's full size (N=768, c_z=128), every output."""
+    n = 768
+    log("front end n=768")
+    x = inputs.block_inputs(n, seed=4)
+    gr = inputs.proj_grad_inputs(n, seed=6)
+    xd, gd = dev(x, device), dev(gr, device)
+    q, k, v, gate, bias, mean, rstd = ta.ln_proj_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"])
+    got = ta.ln_proj_bwd(xd["z"], xd["gamma"], xd["beta"], mean, rstd, xd["w_qkvg"], xd["w_bias"], gd["dq"], gd["dk"],
+                         gd["dv"], gd["dgate"], gd["dbias"])
+    torch.cuda.synchronize()
+    ref = B.ln_proj_fwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], H, C)
+    for name, t in dict(q=q, k=k, v=v, gate=gate, bias=bias).items():
+        assert_close(f"n768:{name}", t.cpu(), ref[name], TOL)
+    del ref
+    ref = B.ln_proj_bwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], gr["dq"], gr["dk"], gr["dv"],
+                        gr["dgate"], gr["dbias"], H, C)
+    for name, t in zip(("dz", "dgamma", "dbeta", "dw_qkvg", "dw_bias"), got):
+        assert_close(f"n768:{name}", t.cpu(), ref[name], TOL)
+
+
+def test_block_determinism(device):
+    n = 96
+    log("block determinism")
+    xd = dev(inputs.block_inputs(n, seed=60, affine=True), device)
+    runs = []
+    for _ in range(3):
+        y, saved = ta.block_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"])
+        g = ta.block_bwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"], saved, xd["dy"])
+        runs.append(dict(y=y, **g))
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        for key in runs[0]:
+            assert torch.equal(runs[0][key], r[key]), key

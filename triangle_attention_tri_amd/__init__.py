@@ -6,6 +6,8 @@ kernels.  PyTorch provides device memory and the stream.
 
     out, attn, lse = fwd(q, k, v, bias, gate, mask=None, ending=False)
     dq, dk, dv, dbias, dgate = bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending=False)
+    y, saved = block_fwd(z, gamma, beta, w_qkvg, w_bias, w_o, ending=False)   # LN + projections + attention + linear
+    grads = block_bwd(z, gamma, beta, w_qkvg, w_bias, w_o, saved, dy, ending=False)
 
 Layouts (starting node, N tokens, H heads, c = 32):
     q, k, v [N,H,N,c]; bias [H,N,N]; gate, out, dout [N,N,H,c]; mask [N,N] uint8
@@ -19,7 +21,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_size", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path", "load"]
+__all__ = ["fwd", "bwd", "workspace_size", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path",
+           "load", "ln_proj_fwd", "ln_proj_bwd", "out_proj_fwd", "out_proj_bwd", "block_fwd", "block_bwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtri_attn.so")
@@ -52,6 +55,19 @@ def load():
     lib.tri_attn_bwd_workspace_size.restype = sz
     lib.tri_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
     lib.tri_attn_bwd.restype = i
+    f = ctypes.c_float
+    lib.tri_attn_ln_proj_fwd.argtypes = [i] * 6 + [vp, vp, vp, f] + [vp] * 9 + [vp]
+    lib.tri_attn_ln_proj_fwd.restype = i
+    lib.tri_attn_ln_proj_bwd_workspace_size.argtypes = [i] * 6
+    lib.tri_attn_ln_proj_bwd_workspace_size.restype = sz
+    lib.tri_attn_ln_proj_bwd.argtypes = [i] * 6 + [vp] * 17 + [vp, sz, vp]
+    lib.tri_attn_ln_proj_bwd.restype = i
+    lib.tri_attn_out_proj_fwd.argtypes = [i] * 4 + [vp] * 3 + [vp]
+    lib.tri_attn_out_proj_fwd.restype = i
+    lib.tri_attn_out_proj_bwd_workspace_size.argtypes = [i] * 4
+    lib.tri_attn_out_proj_bwd_workspace_size.restype = sz
+    lib.tri_attn_out_proj_bwd.argtypes = [i] * 4 + [vp] * 5 + [vp, sz, vp]
+    lib.tri_attn_out_proj_bwd.restype = i
     _lib = lib
     return lib
 
@@ -162,6 +178,114 @@ def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, worksp
                           _stream(q.device))
     _check(st, "tri_attn_bwd")
     return dq, dk, dv, dbias, dgate
+
+
+# ---------------------------------------------------------------------------
+# LayerNorm + projection front end and output linear (bf16, c_z = h*c = 128)
+
+def ln_proj_fwd(z, gamma, beta, w_qkvg, w_bias, h: int = 4, c: int = 32, eps: float = 1e-5):
+    """z [R,N,cz] -> (q, k, v [R,h,N,c], gate [R,N,h,c], bias [h,R,N], mean, rstd [R,N] fp32).
+
+    For R < N (a slice of pair rows) ``bias`` is returned as [h,R,N]; the C ABI
+    itself can also write into a full [h,N,N] tensor at a row offset.
+    """
+    import torch
+    lib = load()
+    n_rows, n, cz = z.shape
+    _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias), torch.bfloat16, z.device)
+    dev = z.device
+    q = torch.empty((n_rows, h, n, c), dtype=z.dtype, device=dev)
+    k, v = torch.empty_like(q), torch.empty_like(q)
+    gate = torch.empty((n_rows, n, h, c), dtype=z.dtype, device=dev)
+    bias = torch.empty((h, n_rows, n), dtype=z.dtype, device=dev) if n_rows == n else None
+    mean = torch.empty((n_rows, n), dtype=torch.float32, device=dev)
+    rstd = torch.empty_like(mean)
+    if bias is None:
+        raise ValueError("row slices: call the C ABI with the full bias tensor at a row offset")
+    st = lib.tri_attn_ln_proj_fwd(n_rows, n, cz, h, c, BF16, _ptr(z), _ptr(gamma), _ptr(beta), ctypes.c_float(eps),
+                                  _ptr(w_qkvg), _ptr(w_bias), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(bias),
+                                  _ptr(mean), _ptr(rstd), _stream(dev))
+    _check(st, "tri_attn_ln_proj_fwd")
+    return q, k, v, gate, bias, mean, rstd
+
+
+def ln_proj_bwd(z, gamma, beta, mean, rstd, w_qkvg, w_bias, dq, dk, dv, dgate, dbias, h: int = 4, c: int = 32,
+                workspace=None):
+    """Returns (dz, dgamma, dbeta, dw_qkvg, dw_bias)."""
+    import torch
+    lib = load()
+    n_rows, n, cz = z.shape
+    _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, dq=dq, dk=dk, dv=dv, dgate=dgate,
+               dbias=dbias), torch.bfloat16, z.device)
+    need = int(lib.tri_attn_ln_proj_bwd_workspace_size(n_rows, n, cz, h, c, BF16))
+    if need == 0:
+        _check(-2, "tri_attn_ln_proj_bwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+    dz = torch.empty_like(z)
+    dgamma, dbeta = torch.empty_like(gamma), torch.empty_like(beta)
+    dw_qkvg, dw_bias = torch.empty_like(w_qkvg), torch.empty_like(w_bias)
+    st = lib.tri_attn_ln_proj_bwd(n_rows, n, cz, h, c, BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(mean),
+                                  _ptr(rstd), _ptr(w_qkvg), _ptr(w_bias), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgate),
+                                  _ptr(dbias), _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(dw_qkvg), _ptr(dw_bias),
+                                  _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(z.device))
+    _check(st, "tri_attn_ln_proj_bwd")
+    return dz, dgamma, dbeta, dw_qkvg, dw_bias
+
+
+def out_proj_fwd(o, w_o):
+    """o [..., h, c] (pairs first) -> y [..., c_out] = o.flatten(-2) @ w_o.T."""
+    import torch
+    lib = load()
+    c_out, c_in = w_o.shape
+    n_pairs = o.numel() // c_in
+    _prep(dict(o=o, w_o=w_o), torch.bfloat16, o.device)
+    y = torch.empty(o.shape[:-2] + (c_out,), dtype=o.dtype, device=o.device)
+    st = lib.tri_attn_out_proj_fwd(n_pairs, c_in, c_out, BF16, _ptr(o), _ptr(w_o), _ptr(y), _stream(o.device))
+    _check(st, "tri_attn_out_proj_fwd")
+    return y
+
+
+def out_proj_bwd(o, w_o, dy, workspace=None):
+    """Returns (do, dw_o)."""
+    import torch
+    lib = load()
+    c_out, c_in = w_o.shape
+    n_pairs = o.numel() // c_in
+    _prep(dict(o=o, w_o=w_o, dy=dy), torch.bfloat16, o.device)
+    need = int(lib.tri_attn_out_proj_bwd_workspace_size(n_pairs, c_in, c_out, BF16))
+    if need == 0:
+        _check(-2, "tri_attn_out_proj_bwd_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=o.device)
+    d_o = torch.empty_like(o)
+    dw_o = torch.empty_like(w_o)
+    st = lib.tri_attn_out_proj_bwd(n_pairs, c_in, c_out, BF16, _ptr(o), _ptr(w_o), _ptr(dy), _ptr(d_o), _ptr(dw_o),
+                                   _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(o.device))
+    _check(st, "tri_attn_out_proj_bwd")
+    return d_o, dw_o
+
+
+def block_fwd(z, gamma, beta, w_qkvg, w_bias, w_o, ending: bool = False, mask=None, eps: float = 1e-5):
+    """LayerNorm + projections -> attention (starting or ending node) -> output linear.
+
+    Returns (y, saved) where ``saved`` holds what block_bwd needs.
+    """
+    q, k, v, gate, bias, mean, rstd = ln_proj_fwd(z, gamma, beta, w_qkvg, w_bias, eps=eps)
+    out, attn, lse = fwd(q, k, v, bias, gate, mask, ending)
+    y = out_proj_fwd(out, w_o)
+    return y, dict(q=q, k=k, v=v, gate=gate, bias=bias, mean=mean, rstd=rstd, out=out, attn=attn, lse=lse)
+
+
+def block_bwd(z, gamma, beta, w_qkvg, w_bias, w_o, saved, dy, ending: bool = False, mask=None):
+    """Returns dict(dz, dgamma, dbeta, dw_qkvg, dw_bias, dw_o)."""
+    s = saved
+    d_out, dw_o = out_proj_bwd(s["out"], w_o, dy)
+    dq, dk, dv, dbias, dgate = bwd(s["q"], s["k"], s["v"], s["bias"], s["gate"], mask, s["attn"], s["lse"], d_out,
+                                   ending)
+    dz, dgamma, dbeta, dw_qkvg, dw_bias = ln_proj_bwd(z, gamma, beta, s["mean"], s["rstd"], w_qkvg, w_bias, dq, dk,
+                                                      dv, dgate, dbias)
+    return dict(dz=dz, dgamma=dgamma, dbeta=dbeta, dw_qkvg=dw_qkvg, dw_bias=dw_bias, dw_o=dw_o)
 
 
 def __getattr__(name):

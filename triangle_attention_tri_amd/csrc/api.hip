@@ -2,7 +2,7 @@
 // starting / ending node, workspace sizing and kernel dispatch.  Declared in
 // include/tri_attn.h.
 #include "../../include/tri_attn.h"
-#include "common.hpp"
+#include "proj.hpp"
 
 namespace tri {
 template <typename T, int R> hipError_t launch_fwd(const FwdArgs<T>&, hipStream_t);
@@ -272,6 +272,124 @@ int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending
     if (stage_events[i] == nullptr) return TRI_ATTN_EINVAL;
   return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv,
                   dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, (hipEvent_t*)stage_events);
+}
+
+// ---------------------------------------------------------------------------
+// LayerNorm + projection front end and output linear (bf16, c_z = h*c = 128).
+
+static int check_proj(int n_rows, int n, int cz, int h, int c, int dtype) {
+  if (n_rows < 1 || n < 1 || n_rows > n || cz < 1 || h < 1 || c < 1) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_BF16 || cz != 128 || c != C || h * c != 128) return TRI_ATTN_EUNSUPPORTED;
+  if ((long long)n_rows * n > (1ll << 28)) return TRI_ATTN_EUNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+static bool aligned(const void* p, uintptr_t a) { return p != nullptr && ((uintptr_t)p & (a - 1)) == 0; }
+
+static int check_ws(void* ws, size_t bytes, size_t need) {
+  if (ws == nullptr || bytes < need) return TRI_ATTN_EWORKSPACE;
+  if (((uintptr_t)ws & 255u) != 0) return TRI_ATTN_EINVAL;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_ln_proj_fwd(int n_rows, int n, int cz, int h, int c, int dtype, const void* z, const void* ln_gamma,
+                         const void* ln_beta, float ln_eps, const void* w_qkvg, const void* w_bias, void* q, void* k,
+                         void* v, void* gate, void* bias, float* ln_mean, float* ln_rstd,
+                         tri_attn_stream_t stream) {
+  int st = check_proj(n_rows, n, cz, h, c, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  if (!(ln_eps > 0.0f) || !(ln_eps < 1.0f)) return TRI_ATTN_EINVAL;
+  const void* a16[] = {z, ln_gamma, ln_beta, w_qkvg, w_bias, q, k, v, gate};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  if (!aligned(bias, 2) || !aligned(ln_mean, 4) || !aligned(ln_rstd, 4)) return TRI_ATTN_EINVAL;
+  ProjArgs a{};
+  a.P = n_rows * n;
+  a.n = n;
+  a.hs = (long long)n * n;
+  a.eps = ln_eps;
+  a.x = (const bf16*)z; a.gamma = (const bf16*)ln_gamma; a.beta = (const bf16*)ln_beta;
+  a.w = (const bf16*)w_qkvg; a.wb = (const bf16*)w_bias;
+  a.q = (bf16*)q; a.k = (bf16*)k; a.v = (bf16*)v; a.gate = (bf16*)gate; a.bias = (bf16*)bias;
+  a.mean = ln_mean; a.rstd = ln_rstd;
+  return hip_status(launch_proj_fwd(a, true, (hipStream_t)stream));
+}
+
+size_t tri_attn_ln_proj_bwd_workspace_size(int n_rows, int n, int cz, int h, int c, int dtype) {
+  if (check_proj(n_rows, n, cz, h, c, dtype) != TRI_ATTN_OK) return 0;
+  return align256(proj_workspace_bytes(n_rows * n, true));
+}
+
+int tri_attn_ln_proj_bwd(int n_rows, int n, int cz, int h, int c, int dtype, const void* z, const void* ln_gamma,
+                         const void* ln_beta, const float* ln_mean, const float* ln_rstd, const void* w_qkvg,
+                         const void* w_bias, const void* dq, const void* dk, const void* dv, const void* dgate,
+                         const void* dbias, void* dz, void* dgamma, void* dbeta, void* dw_qkvg, void* dw_bias,
+                         void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  int st = check_proj(n_rows, n, cz, h, c, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  const void* a16[] = {z, ln_gamma, ln_beta, w_qkvg, w_bias, dq, dk, dv, dgate, dz};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  if (!aligned(dbias, 2) || !aligned(ln_mean, 4) || !aligned(ln_rstd, 4) || !aligned(dgamma, 2) ||
+      !aligned(dbeta, 2) || !aligned(dw_qkvg, 2) || !aligned(dw_bias, 2))
+    return TRI_ATTN_EINVAL;
+  st = check_ws(workspace, workspace_bytes, align256(proj_workspace_bytes(n_rows * n, true)));
+  if (st != TRI_ATTN_OK) return st;
+  ProjArgs a{};
+  a.P = n_rows * n;
+  a.n = n;
+  a.hs = (long long)n * n;
+  a.x = (const bf16*)z; a.gamma = (const bf16*)ln_gamma; a.beta = (const bf16*)ln_beta;
+  a.w = (const bf16*)w_qkvg; a.wb = (const bf16*)w_bias;
+  a.mean_in = ln_mean; a.rstd_in = ln_rstd;
+  a.dq = (const bf16*)dq; a.dk = (const bf16*)dk; a.dv = (const bf16*)dv; a.dgate = (const bf16*)dgate;
+  a.dbias = (const bf16*)dbias;
+  a.dx = (bf16*)dz;
+  a.part_w = (float*)workspace;
+  return hip_status(launch_proj_bwd(a, true, (bf16*)dw_qkvg, (bf16*)dw_bias, (bf16*)dgamma, (bf16*)dbeta,
+                                    (hipStream_t)stream));
+}
+
+static int check_out_proj(int n_pairs, int c_in, int c_out, int dtype) {
+  if (n_pairs < 1 || c_in < 1 || c_out < 1) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_BF16 || c_in != 128 || c_out != 128) return TRI_ATTN_EUNSUPPORTED;
+  if (n_pairs > (1 << 28)) return TRI_ATTN_EUNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+int tri_attn_out_proj_fwd(int n_pairs, int c_in, int c_out, int dtype, const void* x, const void* w, void* y,
+                          tri_attn_stream_t stream) {
+  int st = check_out_proj(n_pairs, c_in, c_out, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return TRI_ATTN_EINVAL;
+  ProjArgs a{};
+  a.P = n_pairs;
+  a.n = 1;
+  a.x = (const bf16*)x; a.w = (const bf16*)w; a.y = (bf16*)y;
+  return hip_status(launch_proj_fwd(a, false, (hipStream_t)stream));
+}
+
+size_t tri_attn_out_proj_bwd_workspace_size(int n_pairs, int c_in, int c_out, int dtype) {
+  if (check_out_proj(n_pairs, c_in, c_out, dtype) != TRI_ATTN_OK) return 0;
+  return align256(proj_workspace_bytes(n_pairs, false));
+}
+
+int tri_attn_out_proj_bwd(int n_pairs, int c_in, int c_out, int dtype, const void* x, const void* w, const void* dy,
+                          void* dx, void* dw, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  int st = check_out_proj(n_pairs, c_in, c_out, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw, 2))
+    return TRI_ATTN_EINVAL;
+  st = check_ws(workspace, workspace_bytes, align256(proj_workspace_bytes(n_pairs, false)));
+  if (st != TRI_ATTN_OK) return st;
+  ProjArgs a{};
+  a.P = n_pairs;
+  a.n = 1;
+  a.x = (const bf16*)x; a.w = (const bf16*)w; a.dy = (const bf16*)dy; a.dx = (bf16*)dx;
+  a.part_w = (float*)workspace;
+  return hip_status(launch_proj_bwd(a, false, (bf16*)dw, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
 }  // extern "C"

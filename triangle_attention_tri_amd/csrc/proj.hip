@@ -1,0 +1,522 @@
+// LayerNorm + projection front end and output linear of the pair block, bf16.
+//
+// The pages place the triangle attention inside a pair stack whose remaining
+// time goes to LayerNorm and linear layers (TurboPairFormer news item, "Dove si
+// impiega il tempo"; ScaleFold summary, fused LayerNorm/linear kernels) and
+// advocate fusing them into few kernels (MegaFold explainer, EvoFusion
+// paragraph).  Every pair is independent, so each kernel streams pairs through
+// MFMA tiles of 32 pairs with the (small) weight matrix held in LDS:
+//
+//   proj_fwd_kernel<FRONT>  FRONT: xhat = LN(z) in registers, then
+//                             [q|k|v|gate|bias] = xhat . W^T scattered straight
+//                             into the attention layouts; saves mean / rstd.
+//                           plain: y = o . W_o^T.
+//   proj_dx_kernel<FRONT>   dX = dT . W (dT gathered from the attention-layout
+//                             gradients); FRONT adds the LayerNorm backward
+//                             (dz) and per-wave partial sums of dgamma / dbeta.
+//   proj_dw_kernel<FRONT>   per-workgroup partial dW = dT^T . X over a
+//                             contiguous range of pairs (X = xhat recomputed
+//                             from z with the saved statistics, or o).
+//   proj_sum_kernel         fixed-order sum of the partials (bit-identical
+//                           results from run to run), rounded once to bf16.
+//
+// Channel counts are fixed: c_z = 128 input channels, h * c = 4 * 32 = 128.
+// Pairs are numbered p = a * n + b over the processed rows a.
+#include "proj.hpp"
+
+namespace tri {
+
+namespace {
+
+constexpr int CZ = 128;          // LayerNorm width, projection input
+constexpr int PH = 4;            // heads (h * 32 == 128)
+constexpr int PJ_WAVES = 8;
+constexpr int PJ_THREADS = 64 * PJ_WAVES;
+constexpr int FRONT_M = 544;     // 512 q/k/v/gate rows + one 32-row block holding the PH bias rows
+constexpr int PW_ROW = 136;      // LDS pitch of row-read weight tiles: 16 B bank shift per row
+constexpr int PW_T_FRONT = 552;  // LDS pitch of the transposed front weights (20-bank shift per row)
+constexpr int PW_T_PLAIN = 136;
+constexpr int PD_FRONT = 544;    // pitch of the staged dT tile: row stride == 64 B mod 256 for
+constexpr int PD_PLAIN = 160;    // conflict-free transposing reads
+constexpr int PX = 160;
+constexpr int PROJ_GRID = 256;  // workgroups per launch (one per CU)
+
+}  // namespace
+
+
+
+namespace {
+
+__device__ __forceinline__ void store4(bf16* p, const f32x16& acc, int u) {
+  *reinterpret_cast<bf16x4*>(p) = (bf16x4){(bf16)acc[4 * u], (bf16)acc[4 * u + 1], (bf16)acc[4 * u + 2],
+                                           (bf16)acc[4 * u + 3]};
+}
+
+// LayerNorm output of one channel, the same expression in every kernel so the
+// recomputed xhat is bit-identical to the forward's.
+__device__ __forceinline__ float ln_apply(float z, float mean, float rstd, float gam, float bet) {
+  return (z - mean) * rstd * gam + bet;
+}
+
+// Stage a weight matrix into LDS as rows of PW_ROW elements.  Rows 512.. of the
+// front matrix are the PH bias rows followed by zeros.
+template <bool FRONT>
+__device__ __forceinline__ bf16x8 weight_chunk(const ProjArgs& a, int row, int c8) {
+  if (!FRONT || row < 512) return *reinterpret_cast<const bf16x8*>(a.w + row * CZ + c8);
+  if (row - 512 < PH) return *reinterpret_cast<const bf16x8*>(a.wb + (row - 512) * CZ + c8);
+  return (bf16x8)(0);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+template <bool FRONT>
+__global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int M = FRONT ? FRONT_M : 128;
+  bf16* sW = reinterpret_cast<bf16*>(smem);
+  float* sG = reinterpret_cast<float*>(smem + M * PW_ROW * 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  for (int q = tid; q < M * 16; q += PJ_THREADS) {
+    const int row = q >> 4, c8 = (q & 15) * 8;
+    *reinterpret_cast<bf16x8*>(sW + row * PW_ROW + c8) = weight_chunk<FRONT>(a, row, c8);
+  }
+  if (FRONT && tid < CZ) {
+    sG[tid] = (float)a.gamma[tid];
+    sG[CZ + tid] = (float)a.beta[tid];
+  }
+  __syncthreads();
+
+  const int ntile = (a.P + 31) / 32;
+  for (int t = blockIdx.x * PJ_WAVES + wave; t < ntile; t += gridDim.x * PJ_WAVES) {
+    const int p = t * 32 + l32;
+    const bool live = p < a.P;
+    const int pc = live ? p : a.P - 1;
+    // B operands: lane holds channels 32kb + 16u + 8g + e of its pair
+    Op<bf16> xo[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) xo[kb] = load_c_op(a.x + (long long)pc * CZ + 32 * kb, g);
+    if constexpr (FRONT) {
+      float s = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) s += (float)xo[kb].f[u][e];
+      s += __shfl_xor(s, 32);
+      const float mean = s * (1.0f / CZ);
+      float d = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const float t0 = (float)xo[kb].f[u][e] - mean;
+            d += t0 * t0;
+          }
+      d += __shfl_xor(d, 32);
+      const float rstd = 1.0f / sqrtf(d * (1.0f / CZ) + a.eps);
+      if (live && g == 0) {
+        a.mean[p] = mean;
+        a.rstd[p] = rstd;
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+        for (int u = 0; u < 2; u++)
+#pragma unroll
+          for (int e = 0; e < 8; e++) {
+            const int ch = 32 * kb + 16 * u + 8 * g + e;
+            xo[kb].f[u][e] = (bf16)ln_apply((float)xo[kb].f[u][e], mean, rstd, sG[ch], sG[CZ + ch]);
+          }
+    }
+    const int ia = FRONT ? pc / a.n : 0, ib = FRONT ? pc - ia * a.n : 0;
+    // one output block at a time: unrolling hoists the weight reads of several
+    // blocks and spills; the two waves per SIMD overlap each other's MFMA chains
+#pragma unroll 1
+    for (int oc = 0; oc < M / 32; oc++) {
+      f32x16 acc = zero16();
+#pragma unroll
+      for (int kb = 0; kb < 4; kb++) acc = mma32(lds_c_op(sW + (oc * 32 + l32) * PW_ROW + 32 * kb, g), xo[kb], acc);
+      // acc[r]: output channel oc*32 + mrow(g, r) of pair p
+      if (!live) {
+      } else if constexpr (FRONT) {
+        const int sel = oc / PH, hh = oc % PH;
+        if (sel < 3) {
+          bf16* dst = sel == 0 ? a.q : sel == 1 ? a.k : a.v;
+          bf16* base = dst + (((long long)ia * PH + hh) * a.n + ib) * 32 + 4 * g;
+#pragma unroll
+          for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
+        } else if (sel == 3) {
+          bf16* base = a.gate + ((long long)p * PH + hh) * 32 + 4 * g;
+#pragma unroll
+          for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
+        } else if (g == 0) {
+#pragma unroll
+          for (int e = 0; e < PH; e++) a.bias[e * a.hs + p] = (bf16)acc[e];
+        }
+      } else {
+        bf16* base = a.y + (long long)p * CZ + oc * 32 + 4 * g;
+#pragma unroll
+        for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dT gather for one 32-channel block kb of pair pc: lane holds channels
+// 32kb + 16u + 8g + e.
+template <bool FRONT>
+__device__ __forceinline__ Op<bf16> gather_dt(const ProjArgs& a, int kb, int pc, int ia, int ib, int g) {
+  if constexpr (!FRONT) {
+    return load_c_op(a.dy + (long long)pc * CZ + 32 * kb, g);
+  } else {
+    if (kb < 12) {
+      const bf16* src = kb < 4 ? a.dq : kb < 8 ? a.dk : a.dv;
+      return load_c_op(src + (((long long)ia * PH + (kb & 3)) * a.n + ib) * 32, g);
+    }
+    if (kb < 16) return load_c_op(a.dgate + ((long long)pc * PH + (kb - 12)) * 32, g);
+    Op<bf16> o = zero_op<bf16>();
+    if (g == 0) {
+#pragma unroll
+      for (int e = 0; e < PH; e++) o.f[0][e] = a.dbias[e * a.hs + pc];
+    }
+    return o;
+  }
+}
+
+template <bool FRONT>
+__global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int M = FRONT ? FRONT_M : 128;
+  constexpr int PT = FRONT ? PW_T_FRONT : PW_T_PLAIN;
+  bf16* sWT = reinterpret_cast<bf16*>(smem);  // [128 input channels][PT]: W transposed
+  float* sG = reinterpret_cast<float*>(smem + CZ * PT * 2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  for (int q = tid; q < M * 16; q += PJ_THREADS) {
+    const int row = q >> 4, c8 = (q & 15) * 8;
+    const bf16x8 val = weight_chunk<FRONT>(a, row, c8);
+#pragma unroll
+    for (int e = 0; e < 8; e++) sWT[(c8 + e) * PT + row] = val[e];
+  }
+  if (FRONT && tid < CZ) sG[tid] = (float)a.gamma[tid];
+  __syncthreads();
+
+  float gacc[2] = {0.0f, 0.0f}, bacc[2] = {0.0f, 0.0f};
+  const int ntile = (a.P + 31) / 32;
+  for (int t = blockIdx.x * PJ_WAVES + wave; t < ntile; t += gridDim.x * PJ_WAVES) {
+    const int p = t * 32 + l32;
+    const bool live = p < a.P;
+    const int pc = live ? p : a.P - 1;
+    const int ia = FRONT ? pc / a.n : 0, ib = FRONT ? pc - ia * a.n : 0;
+    f32x16 acc[4];
+#pragma unroll
+    for (int ch = 0; ch < 4; ch++) acc[ch] = zero16();
+    // the next block's gradient gather is in flight while this block's MFMAs run
+    Op<bf16> bnext = gather_dt<FRONT>(a, 0, pc, ia, ib, g);
+#pragma unroll 1
+    for (int kb = 0; kb < M / 32; kb++) {
+      const Op<bf16> bop = bnext;
+      if (kb + 1 < M / 32) bnext = gather_dt<FRONT>(a, kb + 1, pc, ia, ib, g);
+#pragma unroll
+      for (int ch = 0; ch < 4; ch++) acc[ch] = mma32(lds_c_op(sWT + (ch * 32 + l32) * PT + 32 * kb, g), bop, acc[ch]);
+    }
+    // acc[ch][r]: gradient of input channel ch*32 + mrow(g, r) of pair p
+    if constexpr (!FRONT) {
+      if (live) {
+        bf16* base = a.dx + (long long)p * CZ + 4 * g;
+#pragma unroll
+        for (int ch = 0; ch < 4; ch++)
+#pragma unroll
+          for (int u = 0; u < 4; u++) store4(base + ch * 32 + 8 * u, acc[ch], u);
+      }
+    } else {
+      const float mean = a.mean_in[pc], rstd = a.rstd_in[pc];
+      // xn: normalised input of the lane's 64 channels j -> ch*32 + 8u + 4g + e
+      float xn[64];
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int ch = 0; ch < 4; ch++)
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+          const int c0 = ch * 32 + 8 * u + 4 * g;
+          const bf16x4 z4 = *reinterpret_cast<const bf16x4*>(a.x + (long long)pc * CZ + c0);
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const int j = ch * 16 + u * 4 + e;
+            xn[j] = ((float)z4[e] - mean) * rstd;
+            const float gm = acc[ch][4 * u + e] * sG[c0 + e];
+            s1 += gm;
+            s2 += gm * xn[j];
+          }
+        }
+      s1 += __shfl_xor(s1, 32);
+      s2 += __shfl_xor(s2, 32);
+      const float m1 = s1 * (1.0f / CZ), m2 = s2 * (1.0f / CZ);
+      if (live) {
+        bf16* base = a.dx + (long long)p * CZ + 4 * g;
+#pragma unroll
+        for (int ch = 0; ch < 4; ch++)
+#pragma unroll
+          for (int u = 0; u < 4; u++) {
+            const int c0 = ch * 32 + 8 * u + 4 * g;
+            float d[4];
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+              const int j = ch * 16 + u * 4 + e;
+              d[e] = rstd * (acc[ch][4 * u + e] * sG[c0 + e] - m1 - xn[j] * m2);
+            }
+            *reinterpret_cast<bf16x4*>(base + ch * 32 + 8 * u) = (bf16x4){(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+          }
+      }
+      // dgamma / dbeta of this tile: sum over the 32 pairs (lanes of one half)
+      // by recursive halving, in place (xn becomes the dgamma terms, acc the
+      // dbeta terms); afterwards lane l32 holds entries j = 2*l32, 2*l32+1.
+#pragma unroll
+      for (int j = 0; j < 64; j++) {
+        const float dxv = live ? acc[j >> 4][j & 15] : 0.0f;
+        xn[j] = dxv * xn[j];
+        acc[j >> 4][j & 15] = dxv;
+      }
+#pragma unroll
+      for (int step = 0; step < 5; step++) {
+        const int mask = 16 >> step, half = 32 >> step;
+        const bool up = (l32 & mask) != 0;
+#pragma unroll
+        for (int i = 0; i < half; i++) {
+          const float g_lo = xn[i], g_hi = xn[i + half];
+          const float b_lo = acc[i >> 4][i & 15], b_hi = acc[(i + half) >> 4][(i + half) & 15];
+          xn[i] = (up ? g_hi : g_lo) + __shfl_xor(up ? g_lo : g_hi, mask);
+          acc[i >> 4][i & 15] = (up ? b_hi : b_lo) + __shfl_xor(up ? b_lo : b_hi, mask);
+        }
+      }
+      gacc[0] += xn[0];
+      gacc[1] += xn[1];
+      bacc[0] += acc[0][0];
+      bacc[1] += acc[0][1];
+    }
+  }
+  if constexpr (FRONT) {
+    float* dst = a.part_ln + (long long)(blockIdx.x * PJ_WAVES + wave) * 2 * CZ;
+#pragma unroll
+    for (int jj = 0; jj < 2; jj++) {
+      const int j = 2 * l32 + jj;
+      const int c0 = (j >> 4) * 32 + ((j >> 2) & 3) * 8 + 4 * g + (j & 3);
+      dst[c0] = gacc[jj];
+      dst[CZ + c0] = bacc[jj];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <bool FRONT>
+__global__ __launch_bounds__(PJ_THREADS, 1) void proj_dw_kernel(ProjArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  constexpr int M = FRONT ? FRONT_M : 128;
+  constexpr int PD = FRONT ? PD_FRONT : PD_PLAIN;
+  constexpr int NB = (M / 32) * 4;       // 32x32 blocks of dW
+  constexpr int BPW = (NB + PJ_WAVES - 1) / PJ_WAVES;
+  constexpr int DCH = M / 8 / 16;        // full 16-byte chunks per thread per pair row (16 threads a pair)
+  bf16* sD = reinterpret_cast<bf16*>(smem);             // [2][32][PD]
+  bf16* sX = sD + 2 * 32 * PD;                          // [2][32][PX]
+  float* sG = reinterpret_cast<float*>(sX + 2 * 32 * PX);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (FRONT && tid < CZ) {
+    sG[tid] = (float)a.gamma[tid];
+    sG[CZ + tid] = (float)a.beta[tid];
+  }
+  const int ntile = (a.P + 31) / 32;
+  const int per = (ntile + gridDim.x - 1) / gridDim.x;
+  const int t0 = blockIdx.x * per, t1 = min(ntile, t0 + per);
+  const int pl = tid >> 4, sub = tid & 15;  // staging: 16 threads per pair
+
+  V16 dpre[DCH];
+  V16 xpre;
+  bf16x4 bpre = (bf16x4)(0);
+  float mpre = 0.0f, rpre = 0.0f;
+  bool lpre = false;
+  auto issue = [&](int t) __attribute__((always_inline)) {
+    const int p = t * 32 + pl;
+    lpre = p < a.P;
+    const int pc = lpre ? p : a.P - 1;
+    if constexpr (FRONT) {
+      const int ia = pc / a.n, ib = pc - ia * a.n;
+#pragma unroll
+      for (int s = 0; s < DCH; s++) {
+        const int kb = (sub >> 2) + 4 * s, off = (sub & 3) * 8;  // channel 32kb + off
+        const bf16* src = kb < 12 ? (kb < 4 ? a.dq : kb < 8 ? a.dk : a.dv) +
+                                        (((long long)ia * PH + (kb & 3)) * a.n + ib) * 32 + off
+                                  : a.dgate + ((long long)pc * PH + (kb - 12)) * 32 + off;
+        dpre[s] = *reinterpret_cast<const V16*>(src);
+      }
+      if (sub == 0) {
+#pragma unroll
+        for (int e = 0; e < PH; e++) bpre[e] = a.dbias[e * a.hs + pc];
+      }
+      mpre = a.mean_in[pc];
+      rpre = a.rstd_in[pc];
+    } else {
+      dpre[0] = *reinterpret_cast<const V16*>(a.dy + (long long)pc * CZ + 8 * sub);
+    }
+    xpre = *reinterpret_cast<const V16*>(a.x + (long long)pc * CZ + 8 * sub);
+  };
+  auto stash = [&](int buf) __attribute__((always_inline)) {
+    bf16* d = sD + (buf * 32 + pl) * PD;
+#pragma unroll
+    for (int s = 0; s < DCH; s++) {
+      const int kb = (sub >> 2) + 4 * s, off = (sub & 3) * 8;
+      *reinterpret_cast<V16*>(d + 32 * kb + off) = lpre ? dpre[s] : (V16)(0u);
+    }
+    if constexpr (FRONT) {
+      if (sub < 4) {  // the bias block: PH values then zeros
+        bf16x8 b = (bf16x8)(0);
+        if (sub == 0 && lpre) {
+#pragma unroll
+          for (int e = 0; e < PH; e++) b[e] = bpre[e];
+        }
+        *reinterpret_cast<bf16x8*>(d + 512 + 8 * sub) = b;
+      }
+    }
+    bf16x8 xv = __builtin_bit_cast(bf16x8, xpre);
+    if constexpr (FRONT) {
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int ch = 8 * sub + e;
+        xv[e] = (bf16)ln_apply((float)xv[e], mpre, rpre, sG[ch], sG[CZ + ch]);
+      }
+    }
+    if (!lpre) xv = (bf16x8)(0);
+    *reinterpret_cast<bf16x8*>(sX + (buf * 32 + pl) * PX + 8 * sub) = xv;
+  };
+
+  f32x16 acc[BPW];
+#pragma unroll
+  for (int s = 0; s < BPW; s++) acc[s] = zero16();
+  const int ibk = wave & 3;  // every block a wave owns has column block wave % 4
+  __syncthreads();           // gamma / beta visible to stash
+  if (t0 < t1) {
+    issue(t0);
+    stash(0);
+  }
+  __syncthreads();
+  for (int t = t0; t < t1; t++) {
+    const int buf = (t - t0) & 1;
+    if (t + 1 < t1) issue(t + 1);
+    const Op<bf16> bop = lds_tr_op<MAP_C>(sX + buf * 32 * PX + 32 * ibk, PX, lane);
+#pragma unroll
+    for (int s = 0; s < BPW; s++) {
+      const int bidx = wave + PJ_WAVES * s;
+      if (bidx < NB) {
+        const int mb = bidx >> 2;
+        acc[s] = mma32(lds_tr_op<MAP_C>(sD + buf * 32 * PD + 32 * mb, PD, lane), bop, acc[s]);
+      }
+    }
+    if (t + 1 < t1) stash(buf ^ 1);
+    __syncthreads();
+  }
+  // acc[s][r]: dW[32mb + mrow(g, r)][32 ibk + l32] summed over this workgroup's pairs
+  const int g = lane >> 5, l32 = lane & 31;
+  float* dst = a.part_w + (long long)blockIdx.x * M * CZ;
+#pragma unroll
+  for (int s = 0; s < BPW; s++) {
+    const int bidx = wave + PJ_WAVES * s;
+    if (bidx < NB) {
+      const int mb = bidx >> 2;
+#pragma unroll
+      for (int r = 0; r < 16; r++) dst[(mb * 32 + mrow(g, r)) * CZ + ibk * 32 + l32] = acc[s][r];
+    }
+  }
+}
+
+// Fixed-order sum over partial sets: out[e] = sum_{w ascending} part[w*stride + e].
+__global__ __launch_bounds__(256) void proj_sum_kernel(const float* part, int nparts, long long stride, int count,
+                                                       int split, bf16* out0, bf16* out1) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= count) return;
+  float s = 0.0f;
+  for (int w = 0; w < nparts; w++) s += part[(long long)w * stride + e];
+  if (e < split) out0[e] = (bf16)s;
+  else out1[e - split] = (bf16)s;
+}
+
+// ---------------------------------------------------------------------------
+// Host side
+namespace {
+
+template <typename K> hipError_t set_smem(K kernel, size_t bytes) {
+  // the attribute is per kernel and per process; setting it again is harmless
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+constexpr size_t fwd_smem(bool front) { return (size_t)(front ? FRONT_M : 128) * PW_ROW * 2 + 2 * CZ * 4; }
+constexpr size_t dx_smem(bool front) { return (size_t)CZ * (front ? PW_T_FRONT : PW_T_PLAIN) * 2 + CZ * 4; }
+constexpr size_t dw_smem(bool front) {
+  return (size_t)2 * 32 * (front ? PD_FRONT : PD_PLAIN) * 2 + 2 * 32 * PX * 2 + 2 * CZ * 4;
+}
+
+int grid_for(int P) {
+  const int ntile = (P + 31) / 32;
+  return ntile < PROJ_GRID ? ntile : PROJ_GRID;
+}
+
+}  // namespace
+
+size_t proj_workspace_bytes(int P, bool front) {
+  const int grid = grid_for(P);
+  const size_t m = front ? FRONT_M : 128;
+  size_t b = (size_t)grid * m * CZ * 4;
+  if (front) b += (size_t)grid * PJ_WAVES * 2 * CZ * 4;
+  return b;
+}
+
+hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st) {
+  const int grid = grid_for(a.P);
+  hipError_t e;
+  if (front) {
+    if ((e = set_smem(proj_fwd_kernel<true>, fwd_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_fwd_kernel<true>, dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
+  } else {
+    if ((e = set_smem(proj_fwd_kernel<false>, fwd_smem(false))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_fwd_kernel<false>, dim3(grid), dim3(PJ_THREADS), fwd_smem(false), st, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_proj_bwd(ProjArgs a, bool front, bf16* dw0, bf16* dw1, bf16* dgamma, bf16* dbeta,
+                           hipStream_t st) {
+  const int grid = grid_for(a.P);
+  const int m = front ? FRONT_M : 128;
+  hipError_t e;
+  float* part_w = a.part_w;
+  a.part_ln = part_w + (size_t)grid * m * CZ;
+  if (front) {
+    if ((e = set_smem(proj_dx_kernel<true>, dx_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_dx_kernel<true>, dim3(grid), dim3(PJ_THREADS), dx_smem(true), st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = set_smem(proj_dw_kernel<true>, dw_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_dw_kernel<true>, dim3(grid), dim3(PJ_THREADS), dw_smem(true), st, a);
+  } else {
+    if ((e = set_smem(proj_dx_kernel<false>, dx_smem(false))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_dx_kernel<false>, dim3(grid), dim3(PJ_THREADS), dx_smem(false), st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = set_smem(proj_dw_kernel<false>, dw_smem(false))) != hipSuccess) return e;
+    hipLaunchKernelGGL(proj_dw_kernel<false>, dim3(grid), dim3(PJ_THREADS), dw_smem(false), st, a);
+  }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // weights: front rows 0..511 -> dw0 (w_qkvg), rows 512..512+PH-1 -> dw1 (w_bias)
+  const int wcount = front ? (512 + PH) * CZ : 128 * CZ;
+  hipLaunchKernelGGL(proj_sum_kernel, dim3((wcount + 255) / 256), dim3(256), 0, st, part_w, grid,
+                     (long long)m * CZ, wcount, front ? 512 * CZ : wcount, dw0, dw1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (front) {
+    hipLaunchKernelGGL(proj_sum_kernel, dim3(1), dim3(256), 0, st, a.part_ln, grid * PJ_WAVES, (long long)2 * CZ,
+                       2 * CZ, CZ, dgamma, dbeta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace tri

@@ -111,3 +111,13 @@ def block_inputs(n: int, cz: int = 128, h: int = 4, c: int = 32, dtype=torch.bfl
     if dtype != torch.float32:
         out = {key: t.to(dtype) for key, t in out.items()}
     return out
+
+
+def proj_grad_inputs(n: int, h: int = 4, c: int = 32, dtype=torch.bfloat16, seed: int = 5) -> dict:
+    """Seeded upstream gradients of the front end's five outputs, each ~ N(0,1):
+    dq, dk, dv [n,h,n,c], dgate [n,n,h,c], dbias [h,n,n], drawn in that order."""
+    g = torch.Generator().manual_seed(int(seed))
+    out = dict(dq=torch.randn((n, h, n, c), generator=g), dk=torch.randn((n, h, n, c), generator=g),
+               dv=torch.randn((n, h, n, c), generator=g), dgate=torch.randn((n, n, h, c), generator=g),
+               dbias=torch.randn((h, n, n), generator=g))
+    return {key: t.to(dtype) for key, t in out.items()}
