@@ -91,6 +91,97 @@ def cpu_baseline(x, rows: int):
                       f"{dt:.1f} s wall"}
 
 
+def time_block(lib, hip, dev, stream, n, steps, warmup, no_end):
+    """The N x N x 128 block: LayerNorm + projections -> attention -> output linear, fwd + bwd.
+
+    Every buffer is allocated before timing; a step is the six C ABI calls in
+    order, with HIP events between them.
+    """
+    import torch
+
+    import triangle_attention_tri_amd as ta
+    from triangle_attention_tri_amd import inputs
+    H, c, cz = 4, 32, 128
+    x = {k: v.to(dev) for k, v in inputs.block_inputs(n, cz=cz, h=H, c=c, seed=4).items()}
+    e = lambda *shape, dt=torch.bfloat16: torch.empty(shape, dtype=dt, device=dev)  # noqa: E731
+    q, k, v = e(n, H, n, c), e(n, H, n, c), e(n, H, n, c)
+    gate, bias = e(n, n, H, c), e(H, n, n)
+    mean, rstd = e(n, n, dt=torch.float32), e(n, n, dt=torch.float32)
+    out, attn, lse = e(n, n, H, c), e(n, H, n, c), e(n, H, n, dt=torch.float32)
+    y, d_out, dw_o = e(n, n, cz), e(n, n, H, c), e(cz, H * c)
+    dq, dk, dv, dgate, dbias = e(n, H, n, c), e(n, H, n, c), e(n, H, n, c), e(n, n, H, c), e(H, n, n)
+    dz, dgamma, dbeta, dw_qkvg, dw_bias = e(n, n, cz), e(cz), e(cz), e(4 * H * c, cz), e(H, cz)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sz = ctypes.c_size_t
+    npair = n * n
+    ws_front = torch.empty(lib.tri_attn_ln_proj_bwd_workspace_size(n, n, cz, H, c, ta.BF16), dtype=torch.uint8,
+                           device=dev)
+    ws_out = torch.empty(lib.tri_attn_out_proj_bwd_workspace_size(npair, H * c, cz, ta.BF16), dtype=torch.uint8,
+                         device=dev)
+    ws_att = torch.empty(lib.tri_attn_bwd_workspace_size(n, n, H, c, ta.BF16), dtype=torch.uint8, device=dev)
+    ws_fa = torch.empty(lib.tri_attn_fwd_workspace_size(n, n, H, c, ta.BF16), dtype=torch.uint8, device=dev)
+    names = ["front_fwd", "attn_fwd", "out_fwd", "out_bwd", "attn_bwd", "front_bwd"]
+
+    def step(ending, ev):
+        calls = [
+            lambda: lib.tri_attn_ln_proj_fwd(n, n, cz, H, c, ta.BF16, P(x["z"]), P(x["gamma"]), P(x["beta"]),
+                                             ctypes.c_float(1e-5), P(x["w_qkvg"]), P(x["w_bias"]), P(q), P(k), P(v),
+                                             P(gate), P(bias), P(mean), P(rstd), stream),
+            lambda: lib.tri_attn_fwd(n, n, H, c, ta.BF16, ending, P(q), P(k), P(v), P(bias), P(gate), None, P(out),
+                                     P(attn), P(lse), P(ws_fa), sz(ws_fa.numel()), stream),
+            lambda: lib.tri_attn_out_proj_fwd(npair, H * c, cz, ta.BF16, P(out), P(x["w_o"]), P(y), stream),
+            lambda: lib.tri_attn_out_proj_bwd(npair, H * c, cz, ta.BF16, P(out), P(x["w_o"]), P(x["dy"]), P(d_out),
+                                              P(dw_o), P(ws_out), sz(ws_out.numel()), stream),
+            lambda: lib.tri_attn_bwd(n, n, H, c, ta.BF16, ending, P(q), P(k), P(v), P(bias), P(gate), None, P(attn),
+                                     P(lse), P(d_out), P(dq), P(dk), P(dv), P(dbias), P(dgate), P(ws_att),
+                                     sz(ws_att.numel()), stream),
+            lambda: lib.tri_attn_ln_proj_bwd(n, n, cz, H, c, ta.BF16, P(x["z"]), P(x["gamma"]), P(x["beta"]), P(mean),
+                                             P(rstd), P(x["w_qkvg"]), P(x["w_bias"]), P(dq), P(dk), P(dv), P(dgate),
+                                             P(dbias), P(dz), P(dgamma), P(dbeta), P(dw_qkvg), P(dw_bias),
+                                             P(ws_front), sz(ws_front.numel()), stream),
+        ]
+        for i, call in enumerate(calls):
+            if ev is not None:
+                hip.record(ev[i], stream)
+            st = call()
+            assert st == 0, (names[i], st)
+        if ev is not None:
+            hip.record(ev[len(calls)], stream)
+
+    def run(ending):
+        for _ in range(warmup):
+            step(ending, None)
+        torch.cuda.synchronize()
+        evs = [[hip.event() for _ in range(len(names) + 1)] for _ in range(steps)]
+        for s_ in range(steps):
+            step(ending, evs[s_])
+        torch.cuda.synchronize()
+        total = sum(hip.ms(ev[0], ev[-1]) for ev in evs) / steps
+        stages = {nm: sum(hip.ms(ev[i], ev[i + 1]) for ev in evs) / steps for i, nm in enumerate(names)}
+        return total, stages
+
+    ms_start, stages = run(0)
+    ms_end = None if no_end else run(1)[0]
+    attn_flops = 14.0 * n ** 3 * H * c
+    lin_flops = 3 * 2.0 * npair * cz * (4 * H * c + H) + 3 * 2.0 * npair * (H * c) * cz
+    # algorithmic HBM bytes of the block's streaming kernels (each tensor moved once)
+    front_fwd_bytes = npair * (cz * 2 + 4 * H * c * 2 + H * 2 + 8)
+    front_bwd_bytes = npair * (4 * H * c * 2 + H * 2 + cz * 2 + 8 + cz * 2)
+    out_fwd_bytes = npair * (H * c * 2 + cz * 2)
+    out_bwd_bytes = npair * (cz * 2 + H * c * 2 + H * c * 2)
+    gbs = lambda b, ms: round(b / (ms * 1e-3) / 1e9, 1)  # noqa: E731
+    return {
+        "workload": f"block_N{n}_cz{cz}_H{H}_c{c}_bf16", "flops_per_step": attn_flops + lin_flops,
+        "ms_per_step": round(ms_start, 4), "end_node_ms_per_step": None if ms_end is None else round(ms_end, 4),
+        "tflops": round((attn_flops + lin_flops) / (ms_start * 1e-3) / 1e12, 2),
+        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "hbm_gbs": {"front_fwd": gbs(front_fwd_bytes, stages["front_fwd"]),
+                    "front_bwd": gbs(front_bwd_bytes, stages["front_bwd"]),
+                    "out_fwd": gbs(out_fwd_bytes, stages["out_fwd"]),
+                    "out_bwd": gbs(out_bwd_bytes, stages["out_bwd"])},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -99,6 +190,8 @@ def main():
     ap.add_argument("--n", type=int, default=768)
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the LayerNorm + projection + attention + output-linear block timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -201,6 +294,8 @@ def main():
     if not args.no_end:
         end_ms, _ = timed(1, max(3, args.steps // 2), 2)
 
+    block = None if args.no_block else time_block(lib, hip, dev, stream, n, max(3, args.steps // 2), 2, args.no_end)
+
     cpu = None
     if rank == 0 and args.cpu_rows > 0:
         cpu = cpu_baseline(xc, min(args.cpu_rows, n))
@@ -215,6 +310,7 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "end_node_ms_per_step": None if end_ms is None else round(end_ms, 4),
         "roofline": roofline,
+        "block": block,
         "cpu_baseline": cpu,
     }
     if rank == 0:

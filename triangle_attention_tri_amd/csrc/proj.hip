@@ -52,6 +52,27 @@ __device__ __forceinline__ void store4(bf16* p, const f32x16& acc, int u) {
                                            (bf16)acc[4 * u + 3]};
 }
 
+// Store one pair's 32-channel output block from an accumulator tile (lane
+// (pair, g) holds channels 8u + 4g + e in acc[4u + e]) with two 16-byte stores
+// per lane: the two halves of the wave trade four packed bf16 pairs so that
+// lane g holds channels 8g..8g+7 and 16+8g..16+8g+7.
+__device__ __forceinline__ void store_block32(bf16* row, const f32x16& acc, int g) {
+  uint32_t s[8];
+#pragma unroll
+  for (int u = 0; u < 4; u++)
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+      s[2 * u + h] = __builtin_bit_cast(uint32_t, (bf16x2){(bf16)acc[4 * u + 2 * h], (bf16)acc[4 * u + 2 * h + 1]});
+  const uint32_t snd[4] = {g ? s[0] : s[2], g ? s[1] : s[3], g ? s[4] : s[6], g ? s[5] : s[7]};
+  uint32_t rcv[4];
+#pragma unroll
+  for (int k = 0; k < 4; k++) rcv[k] = __shfl_xor(snd[k], 32);
+  const V16 lo = g ? (V16){rcv[0], rcv[1], s[2], s[3]} : (V16){s[0], s[1], rcv[0], rcv[1]};
+  const V16 hi = g ? (V16){rcv[2], rcv[3], s[6], s[7]} : (V16){s[4], s[5], rcv[2], rcv[3]};
+  *reinterpret_cast<V16*>(row + 8 * g) = lo;
+  *reinterpret_cast<V16*>(row + 16 + 8 * g) = hi;
+}
+
 // LayerNorm output of one channel, the same expression in every kernel so the
 // recomputed xhat is bit-identical to the forward's.
 __device__ __forceinline__ float ln_apply(float z, float mean, float rstd, float gam, float bet) {
@@ -88,14 +109,31 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
   __syncthreads();
 
   const int ntile = (a.P + 31) / 32;
-  for (int t = blockIdx.x * PJ_WAVES + wave; t < ntile; t += gridDim.x * PJ_WAVES) {
-    const int p = t * 32 + l32;
-    const bool live = p < a.P;
-    const int pc = live ? p : a.P - 1;
-    // B operands: lane holds channels 32kb + 16u + 8g + e of its pair
+  const int tstride = gridDim.x * PJ_WAVES;
+  // B operands: lane holds channels 32kb + 16u + 8g + e of its pair.  The next
+  // tile's inputs are loaded while this tile computes (clamped, unconditional).
+  auto load_x = [&](int t, Op<bf16>(&dst)[4]) __attribute__((always_inline)) {
+    const int pp = min(t * 32 + l32, a.P - 1);
+#pragma unroll
+    for (int kb = 0; kb < 4; kb++) dst[kb] = load_c_op(a.x + (long long)pp * CZ + 32 * kb, g);
+  };
+  Op<bf16> xnext[4];
+  load_x(blockIdx.x * PJ_WAVES + wave, xnext);
+  // Complete the first prefetch here, so that at the loop head only the
+  // previous iteration's prefetch is outstanding, followed by its stores: the
+  // wait there then need not cover those stores.  0x0F70 = vmcnt(0) with
+  // expcnt / lgkmcnt left at their maxima.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Every store below is unconditional and the chunk loop is straight-line, so
+  // the wait for the prefetched inputs at the top of the next tile counts only
+  // loads (loads and stores share one counter): lanes past the last pair
+  // recompute the last pair and store identical values to the same addresses.
+  for (int t = blockIdx.x * PJ_WAVES + wave; t < ntile; t += tstride) {
+    const int pc = min(t * 32 + l32, a.P - 1);
     Op<bf16> xo[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb++) xo[kb] = load_c_op(a.x + (long long)pc * CZ + 32 * kb, g);
+    for (int kb = 0; kb < 4; kb++) xo[kb] = xnext[kb];
+    load_x(min(t + tstride, ntile - 1), xnext);
     if constexpr (FRONT) {
       float s = 0.0f;
 #pragma unroll
@@ -118,10 +156,8 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
           }
       d += __shfl_xor(d, 32);
       const float rstd = 1.0f / sqrtf(d * (1.0f / CZ) + a.eps);
-      if (live && g == 0) {
-        a.mean[p] = mean;
-        a.rstd[p] = rstd;
-      }
+      // both halves hold the same statistics (a + b == b + a): one writes mean, the other rstd
+      (g == 0 ? a.mean : a.rstd)[pc] = g == 0 ? mean : rstd;
 #pragma unroll
       for (int kb = 0; kb < 4; kb++)
 #pragma unroll
@@ -133,35 +169,31 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
           }
     }
     const int ia = FRONT ? pc / a.n : 0, ib = FRONT ? pc - ia * a.n : 0;
-    // one output block at a time: unrolling hoists the weight reads of several
-    // blocks and spills; the two waves per SIMD overlap each other's MFMA chains
-#pragma unroll 1
+#pragma unroll
     for (int oc = 0; oc < M / 32; oc++) {
       f32x16 acc = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) acc = mma32(lds_c_op(sW + (oc * 32 + l32) * PW_ROW + 32 * kb, g), xo[kb], acc);
-      // acc[r]: output channel oc*32 + mrow(g, r) of pair p
-      if (!live) {
-      } else if constexpr (FRONT) {
+      // acc[r]: output channel oc*32 + mrow(g, r) of pair pc
+      if constexpr (FRONT) {
         const int sel = oc / PH, hh = oc % PH;
         if (sel < 3) {
           bf16* dst = sel == 0 ? a.q : sel == 1 ? a.k : a.v;
-          bf16* base = dst + (((long long)ia * PH + hh) * a.n + ib) * 32 + 4 * g;
-#pragma unroll
-          for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
+          store_block32(dst + (((long long)ia * PH + hh) * a.n + ib) * 32, acc, g);
         } else if (sel == 3) {
-          bf16* base = a.gate + ((long long)p * PH + hh) * 32 + 4 * g;
+          store_block32(a.gate + ((long long)pc * PH + hh) * 32, acc, g);
+        } else {
+          // bias rows 0..PH-1 live in the g = 0 half; lane (pair, g) stores heads 2g, 2g+1
+          float bv[PH];
 #pragma unroll
-          for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
-        } else if (g == 0) {
+          for (int e = 0; e < PH; e++) bv[e] = __shfl(acc[e], l32);
 #pragma unroll
-          for (int e = 0; e < PH; e++) a.bias[e * a.hs + p] = (bf16)acc[e];
+          for (int e = 0; e < 2; e++) a.bias[(2 * g + e) * a.hs + pc] = (bf16)bv[2 * g + e];
         }
       } else {
-        bf16* base = a.y + (long long)p * CZ + oc * 32 + 4 * g;
-#pragma unroll
-        for (int u = 0; u < 4; u++) store4(base + 8 * u, acc, u);
+        store_block32(a.y + (long long)pc * CZ + oc * 32, acc, g);
       }
+      __builtin_amdgcn_sched_barrier(0);  // keep each block's weight reads next to its MFMAs
     }
   }
 }
@@ -179,10 +211,12 @@ __device__ __forceinline__ Op<bf16> gather_dt(const ProjArgs& a, int kb, int pc,
       return load_c_op(src + (((long long)ia * PH + (kb & 3)) * a.n + ib) * 32, g);
     }
     if (kb < 16) return load_c_op(a.dgate + ((long long)pc * PH + (kb - 12)) * 32, g);
+    // every lane loads (no branch); only the g = 0 half keeps the values
     Op<bf16> o = zero_op<bf16>();
-    if (g == 0) {
 #pragma unroll
-      for (int e = 0; e < PH; e++) o.f[0][e] = a.dbias[e * a.hs + pc];
+    for (int e = 0; e < PH; e++) {
+      const bf16 val = a.dbias[e * a.hs + pc];
+      o.f[0][e] = g == 0 ? val : (bf16)0.0f;
     }
     return o;
   }
@@ -226,13 +260,9 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
     }
     // acc[ch][r]: gradient of input channel ch*32 + mrow(g, r) of pair p
     if constexpr (!FRONT) {
-      if (live) {
-        bf16* base = a.dx + (long long)p * CZ + 4 * g;
+      // lanes past the last pair store the last pair's values again (same data, same address)
 #pragma unroll
-        for (int ch = 0; ch < 4; ch++)
-#pragma unroll
-          for (int u = 0; u < 4; u++) store4(base + ch * 32 + 8 * u, acc[ch], u);
-      }
+      for (int ch = 0; ch < 4; ch++) store_block32(a.dx + (long long)pc * CZ + ch * 32, acc[ch], g);
     } else {
       const float mean = a.mean_in[pc], rstd = a.rstd_in[pc];
       // xn: normalised input of the lane's 64 channels j -> ch*32 + 8u + 4g + e
@@ -256,22 +286,21 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
       s1 += __shfl_xor(s1, 32);
       s2 += __shfl_xor(s2, 32);
       const float m1 = s1 * (1.0f / CZ), m2 = s2 * (1.0f / CZ);
-      if (live) {
-        bf16* base = a.dx + (long long)p * CZ + 4 * g;
+      bf16* base = a.dx + (long long)pc * CZ + 4 * g;
 #pragma unroll
-        for (int ch = 0; ch < 4; ch++)
+      for (int ch = 0; ch < 4; ch++)
 #pragma unroll
-          for (int u = 0; u < 4; u++) {
-            const int c0 = ch * 32 + 8 * u + 4 * g;
-            float d[4];
+        for (int u = 0; u < 4; u++)
+          if (live) {
+          const int c0 = ch * 32 + 8 * u + 4 * g;
+          float d[4];
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-              const int j = ch * 16 + u * 4 + e;
-              d[e] = rstd * (acc[ch][4 * u + e] * sG[c0 + e] - m1 - xn[j] * m2);
-            }
-            *reinterpret_cast<bf16x4*>(base + ch * 32 + 8 * u) = (bf16x4){(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+          for (int e = 0; e < 4; e++) {
+            const int j = ch * 16 + u * 4 + e;
+            d[e] = rstd * (acc[ch][4 * u + e] * sG[c0 + e] - m1 - xn[j] * m2);
           }
-      }
+          *reinterpret_cast<bf16x4*>(base + ch * 32 + 8 * u) = (bf16x4){(bf16)d[0], (bf16)d[1], (bf16)d[2], (bf16)d[3]};
+        }
       // dgamma / dbeta of this tile: sum over the 32 pairs (lanes of one half)
       // by recursive halving, in place (xn becomes the dgamma terms, acc the
       // dbeta terms); afterwards lane l32 holds entries j = 2*l32, 2*l32+1.
@@ -300,13 +329,23 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
     }
   }
   if constexpr (FRONT) {
-    float* dst = a.part_ln + (long long)(blockIdx.x * PJ_WAVES + wave) * 2 * CZ;
+    // the eight waves' dgamma / dbeta partials, summed in wave order through
+    // LDS (the weight tile is no longer needed) into one set per workgroup
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(smem);  // [PJ_WAVES][2 * CZ]
 #pragma unroll
     for (int jj = 0; jj < 2; jj++) {
       const int j = 2 * l32 + jj;
       const int c0 = (j >> 4) * 32 + ((j >> 2) & 3) * 8 + 4 * g + (j & 3);
-      dst[c0] = gacc[jj];
-      dst[CZ + c0] = bacc[jj];
+      red[wave * 2 * CZ + c0] = gacc[jj];
+      red[wave * 2 * CZ + CZ + c0] = bacc[jj];
+    }
+    __syncthreads();
+    if (tid < 2 * CZ) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < PJ_WAVES; w++) sum += red[w * 2 * CZ + tid];
+      a.part_ln[(long long)blockIdx.x * 2 * CZ + tid] = sum;
     }
   }
 }
@@ -431,15 +470,33 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dw_kernel(ProjArgs a) {
   }
 }
 
-// Fixed-order sum over partial sets: out[e] = sum_{w ascending} part[w*stride + e].
+// Fixed-order sum over partial sets: out[e] = sum over w of part[w*stride + e].
+// A block covers 64 consecutive e; its four waves take the sets w = wv, wv+4,
+// ... (coalesced loads, eight in flight) and the four wave sums are added in
+// wave order, so the result does not depend on scheduling.
 __global__ __launch_bounds__(256) void proj_sum_kernel(const float* part, int nparts, long long stride, int count,
                                                        int split, bf16* out0, bf16* out1) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= count) return;
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int ec = e < count ? e : count - 1;
   float s = 0.0f;
-  for (int w = 0; w < nparts; w++) s += part[(long long)w * stride + e];
-  if (e < split) out0[e] = (bf16)s;
-  else out1[e - split] = (bf16)s;
+  int w = wv;
+  for (; w + 28 < nparts; w += 32) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; i++) v[i] = part[(long long)(w + 4 * i) * stride + ec];
+#pragma unroll
+    for (int i = 0; i < 8; i++) s += v[i];
+  }
+  for (; w < nparts; w += 4) s += part[(long long)w * stride + ec];
+  red[wv][lane] = s;
+  __syncthreads();
+  if (wv == 0 && e < count) {
+    const float t = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+    if (e < split) out0[e] = (bf16)t;
+    else out1[e - split] = (bf16)t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +525,7 @@ size_t proj_workspace_bytes(int P, bool front) {
   const int grid = grid_for(P);
   const size_t m = front ? FRONT_M : 128;
   size_t b = (size_t)grid * m * CZ * 4;
-  if (front) b += (size_t)grid * PJ_WAVES * 2 * CZ * 4;
+  if (front) b += (size_t)grid * 2 * CZ * 4;
   return b;
 }
 
@@ -508,11 +565,11 @@ hipError_t launch_proj_bwd(ProjArgs a, bool front, bf16* dw0, bf16* dw1, bf16* d
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // weights: front rows 0..511 -> dw0 (w_qkvg), rows 512..512+PH-1 -> dw1 (w_bias)
   const int wcount = front ? (512 + PH) * CZ : 128 * CZ;
-  hipLaunchKernelGGL(proj_sum_kernel, dim3((wcount + 255) / 256), dim3(256), 0, st, part_w, grid,
+  hipLaunchKernelGGL(proj_sum_kernel, dim3((wcount + 63) / 64), dim3(256), 0, st, part_w, grid,
                      (long long)m * CZ, wcount, front ? 512 * CZ : wcount, dw0, dw1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (front) {
-    hipLaunchKernelGGL(proj_sum_kernel, dim3(1), dim3(256), 0, st, a.part_ln, grid * PJ_WAVES, (long long)2 * CZ,
+    hipLaunchKernelGGL(proj_sum_kernel, dim3(2 * CZ / 64), dim3(256), 0, st, a.part_ln, grid, (long long)2 * CZ,
                        2 * CZ, CZ, dgamma, dbeta);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
