@@ -106,7 +106,7 @@ int pick_kpw(int dtype, int n) {
 }
 
 struct WsLayout {
-  size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, total;
+  size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, trash, total;
   int rows, groups, kpw, nsplit;
 };
 
@@ -124,7 +124,8 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     L.bias_prep = after_d;
     L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * sizeof(float));
     L.dq_part = align256(L.tslab + (size_t)n_rows * h * nt * nt * 1024 * es);
-    L.total = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * sizeof(float) : 0));
+    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * sizeof(float) : 0));
+    L.total = align256(L.trash + BWD_TRASH_BYTES);
     return L;
   }
   L.rows = pick_rows(dtype, n);
@@ -172,6 +173,7 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.bias_prep = (float*)(base + L.bias_prep);
   a.tslab = (T*)(base + L.tslab);
   a.dq_part = (float*)(base + L.dq_part);
+  a.trash = (float*)(base + L.trash);
   a.nsplit = L.nsplit;
   hipError_t e;
   if (L.kpw > 0) {

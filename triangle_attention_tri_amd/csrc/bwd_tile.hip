@@ -304,14 +304,23 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
     return (jt < nt && ktl < nkt) ? bias_h + ((long long)jt * nt + kt0 + ktl) * 1024 : bias_zero;
   };
 
+  // Stores with nothing to write (key tiles past the range, queries past n) go
+  // to a scratch area instead of being branched around: loads and stores share
+  // one completion counter, and with a fixed sequence of memory instructions
+  // per iteration the waits for prefetched data count exactly instead of
+  // draining every outstanding store.
+  T* slab_trash = reinterpret_cast<T*>(a.trash) + lane * 16;
+  float* dq_trash = a.trash + 1024 + tid * 4;
+
   issue_q(0);
   stash_q(0, 0);
   f32x16 bnext = load_tile16<T>(bias_ptr(0, w));
   __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing but the loop's own prefetches in flight at its head
 
   for (int jt = 0; jt < nt; jt++) {
     const int b = jt & 1;
-    if (jt + 1 < nt) issue_q(jt + 1);
+    issue_q(jt + 1);  // row indices clamped: the last iteration reloads the last tile, never used
     const T* tq = sQ + (b * 2 + 0) * TILE * KP;
     const T* tda = sQ + (b * 2 + 1) * TILE * KP;
     const float* tl = sLD + (b * 2 + 0) * TILE + 4 * g;
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
       dvt[t] = mma32(dat, pb, dvt[t]);           // [channel][key]
       dkt[t] = mma32(qt, dsb, dkt[t]);           // [channel][key]
       store_dst<T>(wdt + t * TILE * KP, dsb, l32, g);
-      if (ktl < nkt) store_tile_op<T>(slab_row + (jt * nt + ktg) * 1024, dsb);
+      store_tile_op<T>(ktl < nkt ? slab_row + (jt * nt + ktg) * 1024 : slab_trash, dsb);
     }
     wave_sync_lds();
     // phase 2: dQ += dS K over the wave's key tiles
@@ -375,7 +384,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
     float* slot = sDQ + w * 16 * 64 + lane;
 #pragma unroll
     for (int r = 0; r < 16; r++) slot[r * 64] = dq[r];
-    if (jt + 1 < nt) stash_q(b ^ 1, jt + 1);
+    stash_q(b ^ 1, jt + 1);  // after the last tile: fills the unused buffer
     __syncthreads();
     {
       const int r = tid >> 4, l0 = 4 * (tid & 15);
@@ -386,18 +395,18 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
         sum[0] += x[0]; sum[1] += x[1]; sum[2] += x[2]; sum[3] += x[3];
       }
       const int jj = jt * TILE + mrow(l0 >> 5, r), c0 = l0 & 31;
-      if (jj < n) {
-        if (a.nsplit > 1) {
-          *reinterpret_cast<f32x4*>(a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0) = sum;
-        } else {
-          T* dst = a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0;
-          if constexpr (sizeof(T) == 2)
-            *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(sum[0] * INV_SQRT_C), (bf16)(sum[1] * INV_SQRT_C),
-                                                       (bf16)(sum[2] * INV_SQRT_C), (bf16)(sum[3] * INV_SQRT_C)};
-          else
-            *reinterpret_cast<f32x4*>(dst) = (f32x4){sum[0] * INV_SQRT_C, sum[1] * INV_SQRT_C, sum[2] * INV_SQRT_C,
-                                                     sum[3] * INV_SQRT_C};
-        }
+      const bool jv = jj < n;
+      if (a.nsplit > 1) {
+        float* dst = jv ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0 : dq_trash;
+        *reinterpret_cast<f32x4*>(dst) = sum;
+      } else {
+        T* dst = jv ? a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0 : reinterpret_cast<T*>(dq_trash);
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(sum[0] * INV_SQRT_C), (bf16)(sum[1] * INV_SQRT_C),
+                                                     (bf16)(sum[2] * INV_SQRT_C), (bf16)(sum[3] * INV_SQRT_C)};
+        else
+          *reinterpret_cast<f32x4*>(dst) = (f32x4){sum[0] * INV_SQRT_C, sum[1] * INV_SQRT_C, sum[2] * INV_SQRT_C,
+                                                   sum[3] * INV_SQRT_C};
       }
     }
     __syncthreads();

@@ -267,6 +267,8 @@ template <typename T> struct FwdArgs {
   float* bias_prep;  // workspace: sqrt(c)-scaled bias in per-lane tile order
 };
 
+constexpr int BWD_TRASH_BYTES = 8192;
+
 template <typename T> struct BwdArgs {
   Geo geo;
   const T *q, *k, *v, *bias, *gate, *attn, *dout;
@@ -280,6 +282,8 @@ template <typename T> struct BwdArgs {
   float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order, + one zero tile
   T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
   float* dq_part;    // workspace [nsplit][n_rows][H][n][C] fp32 dQ partial per key split (nsplit > 1)
+  float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
+                     // the tile loop's memory instructions do not depend on branches
   int nsplit;        // key-range splits per row in the tile kernel
 };
 
