@@ -11,6 +11,8 @@ template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_
 template <typename T, int R> size_t bwd_main_smem(int n);
 template <typename T, int KPW> hipError_t launch_bwd_tile(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T> size_t tile_smem(int kpw);
+template <int KPW> hipError_t launch_bwd_pair(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+size_t pair_smem(int kpw);
 }  // namespace tri
 
 using namespace tri;
@@ -101,13 +103,13 @@ int pick_kpw(int dtype, int n) {
   const int tps = (nt + ns - 1) / ns, kpw = (tps + 3) / 4;
   const int max_kpw = 2;
   if (kpw > max_kpw) return 0;
-  const size_t smem = dtype == TRI_ATTN_BF16 ? tile_smem<bf16>(kpw) : tile_smem<float>(kpw);
+  const size_t smem = dtype == TRI_ATTN_BF16 ? pair_smem(kpw) : tile_smem<float>(kpw);
   return smem <= LDS_LIMIT ? kpw : 0;
 }
 
 struct WsLayout {
   size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, trash, total;
-  int rows, groups, kpw, nsplit;
+  int rows, groups, kpw, nsplit, slab_rows;
 };
 
 WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
@@ -123,7 +125,9 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     L.nsplit = pick_nsplit(dtype, n);
     L.bias_prep = after_d;
     L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * sizeof(float));
-    L.dq_part = align256(L.tslab + (size_t)n_rows * h * nt * nt * 1024 * es);
+    // bf16 sums the dS tiles of row pairs before storing them
+    L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + 1) / 2 : n_rows;
+    L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);
     L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * sizeof(float) : 0));
     L.total = align256(L.trash + BWD_TRASH_BYTES);
     return L;
@@ -177,10 +181,20 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.nsplit = L.nsplit;
   hipError_t e;
   if (L.kpw > 0) {
-    switch (L.kpw) {
-      case 1: e = launch_bwd_tile<T, 1>(a, st, ev); break;
-      case 2: e = launch_bwd_tile<T, 2>(a, st, ev); break;
-      default: return TRI_ATTN_EUNSUPPORTED;
+    a.slab_rows = L.slab_rows;
+    if constexpr (sizeof(T) == 2) {
+      // bf16: two rows per workgroup (pair-summed dS slabs)
+      switch (L.kpw) {
+        case 1: e = launch_bwd_pair<1>(a, st, ev); break;
+        case 2: e = launch_bwd_pair<2>(a, st, ev); break;
+        default: return TRI_ATTN_EUNSUPPORTED;
+      }
+    } else {
+      switch (L.kpw) {
+        case 1: e = launch_bwd_tile<T, 1>(a, st, ev); break;
+        case 2: e = launch_bwd_tile<T, 2>(a, st, ev); break;
+        default: return TRI_ATTN_EUNSUPPORTED;
+      }
     }
   } else if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
   else if (L.rows == 2) e = launch_bwd_rows<T, 2>(a, st, ev);

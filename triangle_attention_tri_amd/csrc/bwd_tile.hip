@@ -438,6 +438,268 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
   }
 }
 
+// ---------------------------------------------------------------------------
+// Two-row variant (bf16): one workgroup of eight waves per (row pair, head,
+// key range).  Waves 0-3 take row i, waves 4-7 row i + 1, with the same key
+// tiles in the same positions, so that
+//  * the pair-bias gradient slab holds dS_i + dS_{i+1}: half the slab traffic
+//    and half the rows for the reduction to sum (each wave of a pair stores
+//    one half of every tile it shares with its partner, adding the two waves'
+//    rounded dS in row order);
+//  * dQ needs no cross-wave sum: after the one barrier of an iteration each
+//    wave forms a 16 x 16 block of its row's dQ tile over all the key tiles
+//    with 16x16x32 MFMAs, reading the dS^T tiles of its row's four waves
+//    (double-buffered, so the next iteration's phase 1 may overwrite the
+//    other buffer without a second barrier).
+// A row past the last one (odd row count) or with every key masked runs the
+// tile loop with an all-zero key mask (P = dS = 0), so every wave issues the
+// same instruction sequence; its outputs are written after the loop.
+struct PairSmem {
+  static constexpr int KP = TILE + 8;
+  static constexpr size_t tile = 2 * TILE * KP;                        // one bf16 32 x KP tile
+  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)2 * 4 * kpw * tile; }
+  static constexpr size_t qd_bytes = 2 * 2 * 2 * tile;                   // [buffer][row][Q, dA]
+  static constexpr size_t ld_bytes = 2 * 2 * 2 * TILE * sizeof(float);   // [buffer][row][lse, -D]
+  static constexpr __host__ __device__ size_t dt_bytes(int kpw) { return (size_t)2 * 8 * kpw * tile; }
+  static constexpr __host__ __device__ size_t total(int kpw) {
+    return k_bytes(kpw) + qd_bytes + ld_bytes + dt_bytes(kpw);
+  }
+};
+
+// 16x16x32 operand (lane: row/column lane & 15, contraction 8 * (lane >> 4) + 0..7)
+// taken down the rows of a row-major bf16 LDS tile: column col0 + (lane & 15),
+// rows 8 * (lane >> 4) .. +7, via two transposing reads.
+__device__ __forceinline__ bf16x8 lds_tr_op16(const bf16* tile, int pitch, int col0, int lane) {
+  const int G = lane >> 4, jp = lane & 15;
+  const bf16* base = tile + (8 * G + (jp >> 2)) * pitch + col0 + 4 * (jp & 3);
+  const bf16x4 lo = lds_read_tr(base);
+  const bf16x4 hi = lds_read_tr(base + 4 * pitch);
+  return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <int KPW>
+__global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
+  using SM = PairSmem;
+  using T = bf16;
+  constexpr int KP = SM::KP;
+  extern __shared__ __align__(16) char smem[];
+  T* sK = reinterpret_cast<T*>(smem);                                                     // [2][4*KPW][32][KP]
+  T* sQ = reinterpret_cast<T*>(smem + SM::k_bytes(KPW));                                  // [2][2][2][32][KP]
+  float* sLD = reinterpret_cast<float*>(smem + SM::k_bytes(KPW) + SM::qd_bytes);          // [2][2][2][32]
+  T* sDT = reinterpret_cast<T*>(smem + SM::k_bytes(KPW) + SM::qd_bytes + SM::ld_bytes);   // [2][8][KPW][32][KP]
+
+  const Geo& G = a.geo;
+  const int n = G.n, nt = (n + TILE - 1) / TILE;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int rg = w >> 2, ww = w & 3;                       // row of the pair, wave within the row
+  const int npairs = (G.n_rows + 1) / 2;
+  const int item = xcd_item(blockIdx.x, a.nsplit * npairs * G.H);
+  const int split = item % a.nsplit, pr = (item / a.nsplit) % npairs, h = item / (a.nsplit * npairs);
+  const int tps = (nt + a.nsplit - 1) / a.nsplit;
+  const int kt0 = split * tps;
+  const int nkt = min(tps, nt - kt0);
+  const long long headq = (long long)h * n * C;
+  const int row = 2 * pr + rg;
+  const bool rvalid = row < G.n_rows;
+  const int rowc = rvalid ? row : G.n_rows - 1;            // clamped: loads stay in range
+  const long long irow = ((long long)rowc * G.H + h) * n;
+  const T* qrow = a.q + rowc * G.qkv_row + headq;
+  const bool degen = !row_has_valid_key(a.mask, G, rowc, lane);
+  const bool active = rvalid && !degen;
+
+  // K of both rows' key ranges into LDS
+  constexpr int KCH = 2 * 4 * KPW * TILE * 4;              // 16-byte pieces
+  for (int idx = tid; idx < KCH; idx += 512) {
+    const int rr = idx / (4 * KPW * TILE * 4), rem = idx % (4 * KPW * TILE * 4);
+    const int kl = rem / 4, ch = rem % 4, key = kt0 * TILE + kl;
+    const int rrow = min(2 * pr + rr, G.n_rows - 1);
+    V16 val = {0u, 0u, 0u, 0u};
+    if (kl < nkt * TILE && key < n)
+      val = *reinterpret_cast<const V16*>(a.k + rrow * G.qkv_row + headq + key * G.qkv_pos + ch * 8);
+    *reinterpret_cast<V16*>(sK + (rr * 4 * KPW * TILE + kl) * KP + ch * 8) = val;
+  }
+  const T* sKr = sK + rg * 4 * KPW * TILE * KP;           // this row's K tiles
+  Op<T> vb[KPW];
+  uint32_t kbits[KPW];
+  f32x16 dkt[KPW], dvt[KPW];
+#pragma unroll
+  for (int t = 0; t < KPW; t++) {
+    const int ktg = kt0 + t * 4 + ww;
+    const int kk = ktg * TILE + l32;
+    vb[t] = (t * 4 + ww < nkt && kk < n) ? load_c_op(a.v + rowc * G.qkv_row + headq + kk * G.qkv_pos, g)
+                                         : zero_op<T>();
+    kbits[t] = (active && t * 4 + ww < nkt) ? key_bits(a.mask, G, rowc, ktg * TILE, lane) : 0u;
+    dkt[t] = zero16();
+    dvt[t] = zero16();
+  }
+
+  // staging: one 16-byte piece of the two rows' Q / dA tiles per thread, and
+  // (every thread, duplicates hitting the cache) four lse / D values
+  const int q_row = tid >> 8, q_which = (tid >> 7) & 1, q_jr = (tid >> 2) & 31, q_ch = tid & 3;
+  const int q_rowc = min(2 * pr + q_row, G.n_rows - 1);
+  const T* q_base = q_which ? a.dA + ((long long)q_rowc * G.H + h) * n * C : a.q + q_rowc * G.qkv_row + headq;
+  const long long q_pos = q_which ? C : G.qkv_pos;
+  const int l_idx = tid & 31, l_row = l_idx >> 4, l_which = (l_idx >> 3) & 1, l_j = 4 * (l_idx & 7);
+  const float* l_src = (l_which ? a.Dsum : a.lse) + ((long long)min(2 * pr + l_row, G.n_rows - 1) * G.H + h) * n;
+  V16 qpre;
+  f32x4 ldpre;
+  auto issue_q = [&](int jt) __attribute__((always_inline)) {
+    qpre = reinterpret_cast<const V16*>(q_base + min(jt * TILE + q_jr, n - 1) * q_pos)[q_ch];
+#pragma unroll
+    for (int t = 0; t < 4; t++) ldpre[t] = l_src[min(jt * TILE + l_j + t, n - 1)];
+  };
+  auto stash_q = [&](int buf, int jt) __attribute__((always_inline)) {
+    *reinterpret_cast<V16*>(sQ + (((buf * 2 + q_row) * 2 + q_which) * TILE + q_jr) * KP + q_ch * 8) = qpre;
+    if (tid < 32) {
+      const int j0 = jt * TILE + l_j;
+      f32x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; t++) v[t] = l_which == 0 ? (j0 + t < n ? ldpre[t] * LOG2E : POS_INF) : -ldpre[t];
+      *reinterpret_cast<f32x4*>(sLD + ((buf * 2 + l_row) * 2 + l_which) * TILE + l_j) = v;
+    }
+  };
+
+  const float* bias_h = a.bias_prep + (long long)h * nt * nt * 1024 + lane * 16;
+  const float* bias_zero = a.bias_prep + (long long)G.H * nt * nt * 1024 + lane * 16;
+  auto bias_ptr = [&](int jt, int ktl) __attribute__((always_inline)) {
+    return (jt < nt && ktl < nkt) ? bias_h + ((long long)jt * nt + kt0 + ktl) * 1024 : bias_zero;
+  };
+  T* slab_row = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024 + lane * 16 + 8 * rg;
+  T* slab_trash = reinterpret_cast<T*>(a.trash) + lane * 16;
+  float* dq_trash = a.trash + 1024 + tid;
+  // this wave's dQ block: queries 16 qb.., channels 16 cb..
+  const int qb = ww >> 1, cb = ww & 1;
+  const int dq_c = 16 * cb + (lane & 15);
+
+  issue_q(0);
+  stash_q(0, 0);
+  f32x16 bnext = load_tile16<T>(bias_ptr(0, ww));
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
+
+  for (int jt = 0; jt < nt; jt++) {
+    const int b = jt & 1;
+    issue_q(jt + 1);  // clamped rows: the last iteration reloads the last tile, never used
+    const T* tq = sQ + ((b * 2 + rg) * 2 + 0) * TILE * KP;
+    const T* tda = sQ + ((b * 2 + rg) * 2 + 1) * TILE * KP;
+    const float* tl = sLD + ((b * 2 + rg) * 2 + 0) * TILE + 4 * g;
+    const float* td = sLD + ((b * 2 + rg) * 2 + 1) * TILE + 4 * g;
+    const Op<T> qa = lds_c_op(tq + l32 * KP, g);
+    const Op<T> daa = lds_c_op(tda + l32 * KP, g);
+    const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
+    const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
+    T* wdt = sDT + ((b * 8 + w) * KPW) * TILE * KP;
+    // phase 1: per key tile, S and P recomputed once; dV, dK and the dS^T tile
+#pragma unroll
+    for (int t = 0; t < KPW; t++) {
+      const int ktl = t * 4 + ww;
+      const f32x16 bias = bnext;
+      bnext = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, ww));
+      const Op<T> kb = lds_c_op(sKr + (ktl * TILE + l32) * KP, g);
+      const f32x16 s = mma32(qa, kb, bias);
+      f32x16 p;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(tl + 8 * s4);
+#pragma unroll
+        for (int q = 0; q < 4; q++) p[4 * s4 + q] = fast_exp2(__builtin_fmaf(s[4 * s4 + q], SC, -l4[q]));
+      }
+      if (kbits[t] != 0xffffffffu) {
+        const bool kv = (kbits[t] >> l32) & 1u;
+#pragma unroll
+        for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
+      }
+      f32x16 dng;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + 8 * s4);
+#pragma unroll
+        for (int q = 0; q < 4; q++) dng[4 * s4 + q] = d4[q];
+      }
+      const f32x16 dp = mma32(daa, vb[t], dng);
+      f32x16 ds;
+#pragma unroll
+      for (int r = 0; r < 16; r++) ds[r] = p[r] * dp[r];
+      const Op<T> pb = acc_op<T>(p);
+      const Op<T> dsb = acc_op<T>(ds);
+      dvt[t] = mma32(dat, pb, dvt[t]);
+      dkt[t] = mma32(qt, dsb, dkt[t]);
+      store_dst<T>(wdt + t * TILE * KP, dsb, l32, g);
+    }
+    stash_q(b ^ 1, jt + 1);
+    __syncthreads();
+    // phase 2a: dQ block over all key tiles of this row (16x16x32 MFMAs)
+    {
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k8 = 0; k8 < 4 * KPW; k8++) {
+        const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
+        const bf16x8 aop = lds_tr_op16(dtile, KP, 16 * qb, lane);
+        const bf16x8 bop = lds_tr_op16(sKr + k8 * TILE * KP, KP, 16 * cb, lane);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc, 0, 0, 0);
+      }
+      // acc[i]: query jt*32 + 16qb + 4(lane>>4) + i, channel dq_c
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const int jj = jt * TILE + 16 * qb + 4 * (lane >> 4) + i;
+        const bool ok = rvalid && jj < n;
+        if (a.nsplit > 1) {
+          float* dst = ok ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c : dq_trash;
+          *dst = acc[i];
+        } else {
+          T* dst = ok ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : reinterpret_cast<T*>(dq_trash);
+          *dst = (bf16)(acc[i] * INV_SQRT_C);
+        }
+      }
+    }
+    // phase 2b: pair-bias slab = dS of row i + dS of row i+1 (rounded operands,
+    // added in row order); this wave stores half rg of each of its tiles
+#pragma unroll
+    for (int t = 0; t < KPW; t++) {
+      const int ktl = t * 4 + ww;
+      const T* d0 = sDT + ((b * 8 + ww) * KPW + t) * TILE * KP + l32 * KP + 16 * rg + 4 * g;
+      const T* d1 = sDT + ((b * 8 + 4 + ww) * KPW + t) * TILE * KP + l32 * KP + 16 * rg + 4 * g;
+      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(d0), x1 = *reinterpret_cast<const bf16x4*>(d0 + 8);
+      const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(d1), y1 = *reinterpret_cast<const bf16x4*>(d1 + 8);
+      bf16x8 sum;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        sum[e] = (bf16)((float)x0[e] + (float)y0[e]);
+        sum[4 + e] = (bf16)((float)x1[e] + (float)y1[e]);
+      }
+      T* dst = ktl < nkt ? slab_row + (jt * nt + kt0 + ktl) * 1024 : slab_trash;
+      *reinterpret_cast<bf16x8*>(dst) = sum;
+    }
+  }
+
+  // dK and dV of this wave's key tiles (a fully masked row: dV = mean of dA, dK = 0)
+  if (!rvalid) return;
+#pragma unroll
+  for (int t = 0; t < KPW; t++) {
+    const int kk = (kt0 + t * 4 + ww) * TILE + l32;
+    if (t * 4 + ww >= nkt || kk >= n) continue;
+    const long long off = rowc * G.qkv_row + headq + kk * G.qkv_pos;
+    if (degen) {
+      for (int c = 16 * g; c < 16 * g + 16; c++) {
+        float sum = 0.0f;
+        for (int jj = 0; jj < n; jj++) sum += (float)a.dA[(irow + jj) * C + c];
+        a.dv[off + c] = (bf16)(sum / (float)n);
+        a.dk[off + c] = (bf16)0.0f;
+      }
+      continue;
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      const int c0 = 4 * g + 8 * s4;
+      *reinterpret_cast<bf16x4*>(a.dk + off + c0) =
+          (bf16x4){(bf16)(dkt[t][4 * s4] * INV_SQRT_C), (bf16)(dkt[t][4 * s4 + 1] * INV_SQRT_C),
+                   (bf16)(dkt[t][4 * s4 + 2] * INV_SQRT_C), (bf16)(dkt[t][4 * s4 + 3] * INV_SQRT_C)};
+      *reinterpret_cast<bf16x4*>(a.dv + off + c0) =
+          (bf16x4){(bf16)dvt[t][4 * s4], (bf16)dvt[t][4 * s4 + 1], (bf16)dvt[t][4 * s4 + 2], (bf16)dvt[t][4 * s4 + 3]};
+    }
+  }
+}
+
 // dQ = (partial of key range 0 + partial of key range 1 + ...) / sqrt(c), ranges in order.
 template <typename T>
 __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
@@ -479,7 +741,7 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   const T* src = a.tslab + e0;
   int row = 0;
-  for (; row + 4 <= G.n_rows; row += 4) {
+  for (; row + 4 <= a.slab_rows; row += 4) {
     float v[4][4];
 #pragma unroll
     for (int q = 0; q < 4; q++) {
@@ -498,7 +760,7 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
 #pragma unroll
       for (int i = 0; i < 4; i++) s[i] += v[q][i];
   }
-  for (; row < G.n_rows; row++) {
+  for (; row < a.slab_rows; row++) {
 #pragma unroll
     for (int i = 0; i < 4; i++) s[i] += to_f(src[row * per_row + i]);
   }
@@ -551,6 +813,51 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
+
+
+size_t pair_smem(int kpw) { return PairSmem::total(kpw); }
+
+template <int KPW>
+hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* ev) {
+  const Geo& G = a.geo;
+  const int nt = (G.n + TILE - 1) / TILE;
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  const int pre_threads = G.n * G.H * 4;  // per row
+  hipLaunchKernelGGL((bwd_pre_vec_kernel<bf16>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
+                     dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
+  hipLaunchKernelGGL((bwd_bias_prep_kernel<bf16>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
+                     a.bias, a.bias_prep);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  static bool attr_set = false;
+  if (!attr_set) {
+    e = hipFuncSetAttribute((const void*)bwd_pair_kernel<KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)PairSmem::total(KPW));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int npairs = (G.n_rows + 1) / 2;
+  hipLaunchKernelGGL((bwd_pair_kernel<KPW>), dim3(a.nsplit * npairs * G.H), dim3(512), PairSmem::total(KPW), st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  const long long red_threads = (long long)G.H * nt * nt * 256;
+  hipLaunchKernelGGL((dbias_tile_reduce_kernel<bf16>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st,
+                     a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.nsplit > 1) {
+    const long long sum_threads = (long long)G.n_rows * G.H * G.n * C / 4;
+    hipLaunchKernelGGL((dq_sum_kernel<bf16>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  return hipSuccess;
+}
+
+template hipError_t launch_bwd_pair<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_pair<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 
 template hipError_t launch_bwd_tile<bf16, 1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<bf16, 2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);

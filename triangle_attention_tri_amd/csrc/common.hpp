@@ -285,6 +285,7 @@ template <typename T> struct BwdArgs {
   float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
                      // the tile loop's memory instructions do not depend on branches
   int nsplit;        // key-range splits per row in the tile kernel
+  int slab_rows;     // row slabs of dS tiles the dbias reduction sums (rows, or row pairs)
 };
 
 // 16 consecutive floats (64 bytes, 16-byte aligned) as one accumulator tile's
