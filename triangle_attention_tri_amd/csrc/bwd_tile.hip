@@ -532,6 +532,11 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     dkt[t] = zero16();
     dvt[t] = zero16();
   }
+  // every key of the wave's tiles kept (the common case): no per-logit select
+  bool kfull = true;
+#pragma unroll
+  for (int t = 0; t < KPW; t++) kfull = kfull && kbits[t] == 0xffffffffu;
+  kfull = __builtin_amdgcn_readfirstlane(kfull ? 1 : 0) != 0;
 
   // staging: one 16-byte piece of the two rows' Q / dA tiles per thread, and
   // (every thread, duplicates hitting the cache) four lse / D values
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 #pragma unroll
         for (int q = 0; q < 4; q++) p[4 * s4 + q] = fast_exp2(__builtin_fmaf(s[4 * s4 + q], SC, -l4[q]));
       }
-      if (kbits[t] != 0xffffffffu) {
+      if (!kfull) {
         const bool kv = (kbits[t] >> l32) & 1u;
 #pragma unroll
         for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
