@@ -132,3 +132,53 @@ def test_binding_rejects_bad_inputs():
     q = torch.zeros((4, 2, 4, 32), dtype=torch.float16)
     with pytest.raises(TypeError):
         ta.fwd(q, q, q, torch.zeros((2, 4, 4), dtype=torch.float16), torch.zeros((4, 4, 2, 32), dtype=torch.float16))
+
+
+# --- the block entry points (front end, output linear) ----------------------------------
+def call_ln_proj_fwd(lib, n_rows=8, n=8, cz=128, h=4, c=32, dtype=ta.BF16, eps=1e-5, ptrs=None):
+    p = ptrs or [fake_ptr()] * 12
+    return lib.tri_attn_ln_proj_fwd(n_rows, n, cz, h, c, dtype, p[0], p[1], p[2], ctypes.c_float(eps), p[3], p[4],
+                                    p[5], p[6], p[7], p[8], p[9], p[10], p[11], None)
+
+
+def call_ln_proj_bwd(lib, n_rows=8, n=8, cz=128, h=4, c=32, dtype=ta.BF16, ptrs=None, ws_bytes=None, ws=None):
+    p = ptrs or [fake_ptr()] * 17
+    if ws_bytes is None:
+        ws_bytes = lib.tri_attn_ln_proj_bwd_workspace_size(n_rows, n, cz, h, c, dtype)
+    ws = fake_ptr(0x100000) if ws is None else ws
+    return lib.tri_attn_ln_proj_bwd(n_rows, n, cz, h, c, dtype, *p, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def call_out_proj_bwd(lib, n_pairs=64, c_in=128, c_out=128, dtype=ta.BF16, ptrs=None, ws_bytes=None, ws=None):
+    p = ptrs or [fake_ptr()] * 5
+    if ws_bytes is None:
+        ws_bytes = lib.tri_attn_out_proj_bwd_workspace_size(n_pairs, c_in, c_out, dtype)
+    ws = fake_ptr(0x100000) if ws is None else ws
+    return lib.tri_attn_out_proj_bwd(n_pairs, c_in, c_out, dtype, *p, ws, ctypes.c_size_t(ws_bytes), None)
+
+
+def test_block_validation(lib):
+    assert call_ln_proj_fwd(lib, n_rows=0) == EINVAL
+    assert call_ln_proj_fwd(lib, n_rows=9, n=8) == EINVAL
+    assert call_ln_proj_fwd(lib, dtype=3) == EINVAL
+    assert call_ln_proj_fwd(lib, dtype=ta.F32) == EUNSUPPORTED       # bf16 only
+    assert call_ln_proj_fwd(lib, cz=64) == EUNSUPPORTED
+    assert call_ln_proj_fwd(lib, h=2) == EUNSUPPORTED                # h*c must be 128
+    assert call_ln_proj_fwd(lib, eps=0.0) == EINVAL
+    for i in range(12):
+        ptrs = [fake_ptr()] * 12
+        ptrs[i] = None
+        assert call_ln_proj_fwd(lib, ptrs=ptrs) == EINVAL, f"null pointer {i}"
+    assert call_ln_proj_bwd(lib, cz=64) == EUNSUPPORTED
+    assert call_ln_proj_bwd(lib, ws=ctypes.c_void_p(0)) == EWORKSPACE
+    need = lib.tri_attn_ln_proj_bwd_workspace_size(8, 8, 128, 4, 32, ta.BF16)
+    assert need > 0 and need % 256 == 0
+    assert call_ln_proj_bwd(lib, ws_bytes=need - 1) == EWORKSPACE
+    assert call_ln_proj_bwd(lib, ws=fake_ptr(0x100000 + 16)) == EINVAL
+    assert lib.tri_attn_out_proj_fwd(64, 128, 64, ta.BF16, fake_ptr(), fake_ptr(), fake_ptr(), None) == EUNSUPPORTED
+    assert lib.tri_attn_out_proj_fwd(0, 128, 128, ta.BF16, fake_ptr(), fake_ptr(), fake_ptr(), None) == EINVAL
+    assert lib.tri_attn_out_proj_fwd(64, 128, 128, ta.BF16, fake_ptr(2), fake_ptr(), fake_ptr(), None) == EINVAL
+    assert call_out_proj_bwd(lib, c_out=64) == EUNSUPPORTED
+    assert call_out_proj_bwd(lib, ws=ctypes.c_void_p(0)) == EWORKSPACE
+    assert lib.tri_attn_out_proj_bwd_workspace_size(64, 128, 128, ta.BF16) > 0
+    assert lib.tri_attn_ln_proj_bwd_workspace_size(8, 8, 128, 4, 32, ta.F32) == 0
