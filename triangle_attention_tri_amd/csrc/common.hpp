@@ -48,7 +48,8 @@ template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + fast_exp2(-x * LOG2E)); }
+// 1 / (1 + 2^(-x log2 e)) with the hardware reciprocal (about 1 ulp)
+__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-x * LOG2E)); }
 
 // ---------------------------------------------------------------------------
 // MFMA traits
