@@ -576,15 +576,11 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   const int qb = ww >> 1, cb = ww & 1;
   const int dq_c = 16 * cb + (lane & 15);
 
-  issue_q(0);
-  stash_q(0, 0);
-  f32x16 bnext = load_tile16<T>(bias_ptr(0, ww));
-  __syncthreads();
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
-
-  for (int jt = 0; jt < nt; jt++) {
+  f32x16 bnext;
+  // phase 1 of query tile jt: per key tile, S and P recomputed once; dV, dK and
+  // the dS^T tile (buffer jt & 1)
+  auto phase1 = [&](int jt) __attribute__((always_inline)) {
     const int b = jt & 1;
-    issue_q(jt + 1);  // clamped rows: the last iteration reloads the last tile, never used
     const T* tq = sQ + ((b * 2 + rg) * 2 + 0) * TILE * KP;
     const T* tda = sQ + ((b * 2 + rg) * 2 + 1) * TILE * KP;
     const float* tl = sLD + ((b * 2 + rg) * 2 + 0) * TILE + 4 * g;
@@ -594,7 +590,6 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
     const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
     T* wdt = sDT + ((b * 8 + w) * KPW) * TILE * KP;
-    // phase 1: per key tile, S and P recomputed once; dV, dK and the dS^T tile
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
@@ -631,34 +626,35 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       dkt[t] = mma32(qt, dsb, dkt[t]);
       store_dst<T>(wdt + t * TILE * KP, dsb, l32, g);
     }
-    stash_q(b ^ 1, jt + 1);
-    __syncthreads();
-    // phase 2a: dQ block over all key tiles of this row (16x16x32 MFMAs)
-    {
-      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  };
+  // phase 2 of query tile jt (its dS^T tiles complete in buffer jt & 1):
+  // (a) this wave's 16 x 16 dQ block over all key tiles of its row
+  // (16x16x32 MFMAs); (b) the pair-bias slab = dS of row i + dS of row i+1
+  // (rounded operands, added in row order), this wave storing half rg of each
+  // of its tiles
+  auto phase2 = [&](int jt) __attribute__((always_inline)) {
+    const int b = jt & 1;
+    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int k8 = 0; k8 < 4 * KPW; k8++) {
-        const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
-        const bf16x8 aop = lds_tr_op16(dtile, KP, 16 * qb, lane);
-        const bf16x8 bop = lds_tr_op16(sKr + k8 * TILE * KP, KP, 16 * cb, lane);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc, 0, 0, 0);
-      }
-      // acc[i]: query jt*32 + 16qb + 4(lane>>4) + i, channel dq_c
+    for (int k8 = 0; k8 < 4 * KPW; k8++) {
+      const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
+      const bf16x8 aop = lds_tr_op16(dtile, KP, 16 * qb, lane);
+      const bf16x8 bop = lds_tr_op16(sKr + k8 * TILE * KP, KP, 16 * cb, lane);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc, 0, 0, 0);
+    }
+    // acc[i]: query jt*32 + 16qb + 4(lane>>4) + i, channel dq_c
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        const int jj = jt * TILE + 16 * qb + 4 * (lane >> 4) + i;
-        const bool ok = rvalid && jj < n;
-        if (a.nsplit > 1) {
-          float* dst = ok ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c : dq_trash;
-          *dst = acc[i];
-        } else {
-          T* dst = ok ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : reinterpret_cast<T*>(dq_trash);
-          *dst = (bf16)(acc[i] * INV_SQRT_C);
-        }
+    for (int i = 0; i < 4; i++) {
+      const int jj = jt * TILE + 16 * qb + 4 * (lane >> 4) + i;
+      const bool ok = rvalid && jj < n;
+      if (a.nsplit > 1) {
+        float* dst = ok ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c : dq_trash;
+        *dst = acc[i];
+      } else {
+        T* dst = ok ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : reinterpret_cast<T*>(dq_trash);
+        *dst = (bf16)(acc[i] * INV_SQRT_C);
       }
     }
-    // phase 2b: pair-bias slab = dS of row i + dS of row i+1 (rounded operands,
-    // added in row order); this wave stores half rg of each of its tiles
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
@@ -675,7 +671,35 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       T* dst = ktl < nkt ? slab_row + (jt * nt + kt0 + ktl) * 1024 : slab_trash;
       *reinterpret_cast<bf16x8*>(dst) = sum;
     }
+  };
+
+  issue_q(0);
+  stash_q(0, 0);
+  bnext = load_tile16<T>(bias_ptr(0, ww));
+  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
+  issue_q(1);
+  phase1(0);
+  stash_q(1, 1);
+  __syncthreads();
+  // Between two barriers each wave runs phase 1 of tile jt and phase 2 of tile
+  // jt - 1 (whose dS^T tiles sit in the other buffer), row group 0 in that
+  // order and row group 1 in the opposite order: the two waves that share a
+  // SIMD (one of each group) then run different instruction mixes at the same
+  // time instead of competing for the same units.
+  for (int jt = 1; jt < nt; jt++) {
+    issue_q(jt + 1);  // clamped rows: the last iteration reloads the last tile, never used
+    if (rg == 0) {
+      phase1(jt);
+      phase2(jt - 1);
+    } else {
+      phase2(jt - 1);
+      phase1(jt);
+    }
+    stash_q((jt + 1) & 1, jt + 1);
+    __syncthreads();
   }
+  phase2(nt - 1);
 
   // dK and dV of this wave's key tiles (a fully masked row: dV = mean of dA, dK = 0)
   if (!rvalid) return;
