@@ -754,49 +754,55 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
     *reinterpret_cast<f32x4*>(dst) = (f32x4){s[0] * INV_SQRT_C, s[1] * INV_SQRT_C, s[2] * INV_SQRT_C, s[3] * INV_SQRT_C};
 }
 
-// dbias[h][j][k] = sum over rows (ascending) of the per-row dS tiles, fp32.
-// One thread per (h, jt, kt, lane, group of 4 registers).
+// dbias[h][j][k] = sum over slabs (rows or row pairs, ascending) of the dS
+// tiles, fp32, rounded once.  One thread per (h, jt, kt, lane, half of the
+// lane's 16 registers): 16-byte loads (bf16), eight slabs in flight.
+template <typename T>
+__device__ __forceinline__ void load_half_tile(const T* p, float (&v)[8]);
+template <> __device__ __forceinline__ void load_half_tile<bf16>(const bf16* p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; i++) v[i] = (float)x[i];
+}
+template <> __device__ __forceinline__ void load_half_tile<float>(const float* p, float (&v)[8]) {
+  const f32x4 x = *reinterpret_cast<const f32x4*>(p), y = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; i++) { v[i] = x[i]; v[4 + i] = y[i]; }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
-  const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per row of tiles
+  const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per slab
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= per_row / 4) return;
-  const long long e0 = t * 4;  // first element: [h][jt][kt][lane][r0..r0+3]
+  if (t >= per_row / 8) return;
+  const long long e0 = t * 8;  // first element: [h][jt][kt][lane][r0..r0+7]
   const int r0 = (int)(e0 & 15), lane = (int)((e0 >> 4) & 63);
   const long long tile = e0 >> 10;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
-  float s[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   const T* src = a.tslab + e0;
   int row = 0;
-  for (; row + 4 <= a.slab_rows; row += 4) {
-    float v[4][4];
+  for (; row + 8 <= a.slab_rows; row += 8) {
+    float v[8][8];
 #pragma unroll
-    for (int q = 0; q < 4; q++) {
-      if constexpr (sizeof(T) == 2) {
-        const bf16x4 x = *reinterpret_cast<const bf16x4*>(src + (row + q) * per_row);
+    for (int q = 0; q < 8; q++) load_half_tile<T>(src + (row + q) * per_row, v[q]);
 #pragma unroll
-        for (int i = 0; i < 4; i++) v[q][i] = (float)x[i];
-      } else {
-        const f32x4 x = *reinterpret_cast<const f32x4*>(src + (row + q) * per_row);
+    for (int q = 0; q < 8; q++)
 #pragma unroll
-        for (int i = 0; i < 4; i++) v[q][i] = x[i];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; q++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) s[i] += v[q][i];
+      for (int i = 0; i < 8; i++) s[i] += v[q][i];
   }
   for (; row < a.slab_rows; row++) {
+    float v[8];
+    load_half_tile<T>(src + row * per_row, v);
 #pragma unroll
-    for (int i = 0; i < 4; i++) s[i] += to_f(src[row * per_row + i]);
+    for (int i = 0; i < 8; i++) s[i] += v[i];
   }
   const int k = kt * TILE + (lane & 31), g = lane >> 5;
   if (k >= n) return;
 #pragma unroll
-  for (int i = 0; i < 4; i++) {
+  for (int i = 0; i < 8; i++) {
     const int j = jt * TILE + mrow(g, r0 + i);
     if (j < n) a.dbias[(long long)h * n * n + j * G.bias_q + k * G.bias_k] = from_f<T>(s[i]);
   }
@@ -831,7 +837,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
                      st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  const long long red_threads = (long long)G.H * nt * nt * 256;
+  const long long red_threads = (long long)G.H * nt * nt * 128;
   hipLaunchKernelGGL((dbias_tile_reduce_kernel<T>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (a.nsplit > 1) {
@@ -872,7 +878,7 @@ hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* e
   hipLaunchKernelGGL((bwd_pair_kernel<KPW>), dim3(a.nsplit * npairs * G.H), dim3(512), PairSmem::total(KPW), st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  const long long red_threads = (long long)G.H * nt * nt * 256;
+  const long long red_threads = (long long)G.H * nt * nt * 128;
   hipLaunchKernelGGL((dbias_tile_reduce_kernel<bf16>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st,
                      a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
