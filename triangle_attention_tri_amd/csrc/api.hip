@@ -128,7 +128,7 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     // bf16 sums the dS tiles of row pairs before storing them
     L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + 1) / 2 : n_rows;
     L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);
-    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * sizeof(float) : 0));
+    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * es : 0));
     L.total = align256(L.trash + BWD_TRASH_BYTES);
     return L;
   }
@@ -176,7 +176,7 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.groups = L.groups;
   a.bias_prep = (float*)(base + L.bias_prep);
   a.tslab = (T*)(base + L.tslab);
-  a.dq_part = (float*)(base + L.dq_part);
+  a.dq_part = base + L.dq_part;
   a.trash = (float*)(base + L.trash);
   a.nsplit = L.nsplit;
   hipError_t e;

@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
     }
     for (int e = tid; e < n * C; e += 256) {
       const int jj = e / C, c = e % C;
-      if (a.nsplit > 1) a.dq_part[((long long)split * G.n_rows * G.H * n + irow + jj) * C + c] = 0.0f;
+      if (a.nsplit > 1) reinterpret_cast<T*>(a.dq_part)[((long long)split * G.n_rows * G.H * n + irow + jj) * C + c] = from_f<T>(0.0f);
       else a.dq[row * G.qkv_row + headq + jj * G.qkv_pos + c] = from_f<T>(0.0f);
     }
     return;
@@ -397,8 +397,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
       const int jj = jt * TILE + mrow(l0 >> 5, r), c0 = l0 & 31;
       const bool jv = jj < n;
       if (a.nsplit > 1) {
-        float* dst = jv ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0 : dq_trash;
-        *reinterpret_cast<f32x4*>(dst) = sum;
+        // partial of this key range, rounded once to T (summed in fp32 by dq_sum_kernel)
+        T* dst = jv ? reinterpret_cast<T*>(a.dq_part) + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0
+                    : reinterpret_cast<T*>(dq_trash);
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)sum[0], (bf16)sum[1], (bf16)sum[2], (bf16)sum[3]};
+        else
+          *reinterpret_cast<f32x4*>(dst) = sum;
       } else {
         T* dst = jv ? a.dq + row * G.qkv_row + headq + jj * G.qkv_pos + c0 : reinterpret_cast<T*>(dq_trash);
         if constexpr (sizeof(T) == 2)
@@ -648,8 +653,10 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       const int jj = jt * TILE + 16 * qb + 4 * (lane >> 4) + i;
       const bool ok = rvalid && jj < n;
       if (a.nsplit > 1) {
-        float* dst = ok ? a.dq_part + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c : dq_trash;
-        *dst = acc[i];
+        // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
+        T* dst = ok ? reinterpret_cast<T*>(a.dq_part) + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c
+                    : reinterpret_cast<T*>(dq_trash);
+        *dst = (bf16)acc[i];
       } else {
         T* dst = ok ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : reinterpret_cast<T*>(dq_trash);
         *dst = (bf16)(acc[i] * INV_SQRT_C);
@@ -737,10 +744,16 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t * 4 >= per_split) return;
   const long long e = t * 4;
-  f32x4 s = *reinterpret_cast<const f32x4*>(a.dq_part + e);
-  for (int sp = 1; sp < a.nsplit; sp++) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.dq_part + sp * per_split + e);
-    s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
+  const T* part = reinterpret_cast<const T*>(a.dq_part);
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sp = 0; sp < a.nsplit; sp++) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(part + sp * per_split + e);
+      s[0] += (float)x[0]; s[1] += (float)x[1]; s[2] += (float)x[2]; s[3] += (float)x[3];
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * per_split + e);
+      s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
+    }
   }
   const int c0 = (int)(e % C);
   const int jj = (int)((e / C) % G.n);

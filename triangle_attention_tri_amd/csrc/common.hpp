@@ -282,7 +282,7 @@ template <typename T> struct BwdArgs {
   int groups;
   float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order, + one zero tile
   T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
-  float* dq_part;    // workspace [nsplit][n_rows][H][n][C] fp32 dQ partial per key split (nsplit > 1)
+  void* dq_part;     // workspace [nsplit][n_rows][H][n][C] dQ partial per key split (nsplit > 1), in T
   float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
                      // the tile loop's memory instructions do not depend on branches
   int nsplit;        // key-range splits per row in the tile kernel
