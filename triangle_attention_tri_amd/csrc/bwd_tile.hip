@@ -460,8 +460,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
 // tile loop with an all-zero key mask (P = dS = 0), so every wave issues the
 // same instruction sequence; its outputs are written after the loop.
 struct PairSmem {
-  static constexpr int KP = TILE + 8;
-  static constexpr size_t tile = 2 * TILE * KP;                        // one bf16 32 x KP tile
+  static constexpr int KP = TILE;                                      // unpadded rows, swizzled
+  static constexpr size_t tile = 2 * TILE * KP;                        // one bf16 32 x 32 tile
   static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)2 * 4 * kpw * tile; }
   static constexpr size_t qd_bytes = 2 * 2 * 2 * tile;                   // [buffer][row][Q, dA]
   static constexpr size_t ld_bytes = 2 * 2 * 2 * TILE * sizeof(float);   // [buffer][row][lse, -D]
@@ -471,15 +471,63 @@ struct PairSmem {
   }
 };
 
+// LDS swizzles of the 32 x 32 bf16 tiles (64-byte rows, no padding): the
+// element (row r, column c) lives at the returned element offset.  Each makes
+// every access pattern of its tiles free of bank conflicts (64 banks x 4 B):
+//  * swz16 (K, Q, dA tiles: 16-byte row reads and writes, transposing reads):
+//    the 16-byte chunk index is XORed with ((r >> 2) ^ (r >> 4)) & 3;
+//  * swz8 (dS^T tiles: 8-byte row writes / reads, transposing reads): the
+//    8-byte chunk index is XORed with a bit permutation of (r >> 2) & 7.
+// Both keep every 4-element (8-byte) group contiguous, and swz16 every
+// 8-element (16-byte) group.
+__device__ __forceinline__ int swz16(int r, int c) {
+  return r * TILE + ((((c >> 3) ^ (r >> 2) ^ (r >> 4)) & 3) << 3) + (c & 7);
+}
+__device__ __forceinline__ int swz8(int r, int c) {
+  const int a = (r >> 2) & 7;
+  const int t = (((a >> 1) & 1) << 2) | ((a & 1) << 1) | (a >> 2);
+  return r * TILE + ((((c >> 2) ^ t) & 7) << 2) + (c & 3);
+}
+
+// c-map operand of row `row` of a swz16 tile (contraction = the row's columns)
+__device__ __forceinline__ Op<bf16> swz_c_op(const bf16* tile, int row, int g) {
+  Op<bf16> o;
+  o.f[0] = *reinterpret_cast<const bf16x8*>(tile + swz16(row, 8 * g));
+  o.f[1] = *reinterpret_cast<const bf16x8*>(tile + swz16(row, 16 + 8 * g));
+  return o;
+}
+// MAP_M transposed operand of a swz16 tile (see lds_tr_op)
+__device__ __forceinline__ Op<bf16> swz_tr_op_m(const bf16* tile, int lane) {
+  const int G = lane >> 4, jp = lane & 15, g = lane >> 5;
+  const int col = 16 * (G & 1) + 4 * (jp & 3);
+  Op<bf16> o;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const bf16x4 lo = lds_read_tr(tile + swz16(tr_row<MAP_M>(u, 0, g) + (jp >> 2), col));
+    const bf16x4 hi = lds_read_tr(tile + swz16(tr_row<MAP_M>(u, 1, g) + (jp >> 2), col));
+    o.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  return o;
+}
 // 16x16x32 operand (lane: row/column lane & 15, contraction 8 * (lane >> 4) + 0..7)
-// taken down the rows of a row-major bf16 LDS tile: column col0 + (lane & 15),
-// rows 8 * (lane >> 4) .. +7, via two transposing reads.
-__device__ __forceinline__ bf16x8 lds_tr_op16(const bf16* tile, int pitch, int col0, int lane) {
+// taken down the rows of a swizzled tile: column col0 + (lane & 15), rows
+// 8 * (lane >> 4) .. +7, via two transposing reads
+template <bool S8>
+__device__ __forceinline__ bf16x8 swz_tr_op16(const bf16* tile, int col0, int lane) {
   const int G = lane >> 4, jp = lane & 15;
-  const bf16* base = tile + (8 * G + (jp >> 2)) * pitch + col0 + 4 * (jp & 3);
-  const bf16x4 lo = lds_read_tr(base);
-  const bf16x4 hi = lds_read_tr(base + 4 * pitch);
+  const int r = 8 * G + (jp >> 2), c = col0 + 4 * (jp & 3);
+  const bf16x4 lo = lds_read_tr(tile + (S8 ? swz8(r, c) : swz16(r, c)));
+  const bf16x4 hi = lds_read_tr(tile + (S8 ? swz8(r + 4, c) : swz16(r + 4, c)));
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// dS (accumulator order) -> swz8 dS^T tile [key][query]
+__device__ __forceinline__ void swz_store_dst(bf16* tile, const Op<bf16>& o, int l32, int g) {
+#pragma unroll
+  for (int s4 = 0; s4 < 4; s4++) {
+    const int u = s4 >> 1, e0 = 4 * (s4 & 1);
+    *reinterpret_cast<bf16x4*>(tile + swz8(l32, 8 * s4 + 4 * g)) =
+        (bf16x4){o.f[u][e0], o.f[u][e0 + 1], o.f[u][e0 + 2], o.f[u][e0 + 3]};
+  }
 }
 
 template <int KPW>
@@ -521,7 +569,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     V16 val = {0u, 0u, 0u, 0u};
     if (kl < nkt * TILE && key < n)
       val = *reinterpret_cast<const V16*>(a.k + rrow * G.qkv_row + headq + key * G.qkv_pos + ch * 8);
-    *reinterpret_cast<V16*>(sK + (rr * 4 * KPW * TILE + kl) * KP + ch * 8) = val;
+    *reinterpret_cast<V16*>(sK + (rr * 4 * KPW + kl / TILE) * TILE * KP + swz16(kl % TILE, ch * 8)) = val;
   }
   const T* sKr = sK + rg * 4 * KPW * TILE * KP;           // this row's K tiles
   Op<T> vb[KPW];
@@ -559,7 +607,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     for (int t = 0; t < 4; t++) ldpre[t] = l_src[min(jt * TILE + l_j + t, n - 1)];
   };
   auto stash_q = [&](int buf, int jt) __attribute__((always_inline)) {
-    *reinterpret_cast<V16*>(sQ + (((buf * 2 + q_row) * 2 + q_which) * TILE + q_jr) * KP + q_ch * 8) = qpre;
+    *reinterpret_cast<V16*>(sQ + ((buf * 2 + q_row) * 2 + q_which) * TILE * KP + swz16(q_jr, q_ch * 8)) = qpre;
     if (tid < 32) {
       const int j0 = jt * TILE + l_j;
       f32x4 v;
@@ -590,17 +638,17 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const T* tda = sQ + ((b * 2 + rg) * 2 + 1) * TILE * KP;
     const float* tl = sLD + ((b * 2 + rg) * 2 + 0) * TILE + 4 * g;
     const float* td = sLD + ((b * 2 + rg) * 2 + 1) * TILE + 4 * g;
-    const Op<T> qa = lds_c_op(tq + l32 * KP, g);
-    const Op<T> daa = lds_c_op(tda + l32 * KP, g);
-    const Op<T> qt = lds_tr_op<MAP_M>(tq, KP, lane);
-    const Op<T> dat = lds_tr_op<MAP_M>(tda, KP, lane);
+    const Op<T> qa = swz_c_op(tq, l32, g);
+    const Op<T> daa = swz_c_op(tda, l32, g);
+    const Op<T> qt = swz_tr_op_m(tq, lane);
+    const Op<T> dat = swz_tr_op_m(tda, lane);
     T* wdt = sDT + ((b * 8 + w) * KPW) * TILE * KP;
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
       const f32x16 bias = bnext;
       bnext = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, ww));
-      const Op<T> kb = lds_c_op(sKr + (ktl * TILE + l32) * KP, g);
+      const Op<T> kb = swz_c_op(sKr + ktl * TILE * KP, l32, g);
       const f32x16 s = mma32(qa, kb, bias);
       f32x16 p;
 #pragma unroll
@@ -629,7 +677,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       const Op<T> dsb = acc_op<T>(ds);
       dvt[t] = mma32(dat, pb, dvt[t]);
       dkt[t] = mma32(qt, dsb, dkt[t]);
-      store_dst<T>(wdt + t * TILE * KP, dsb, l32, g);
+      swz_store_dst(wdt + t * TILE * KP, dsb, l32, g);
     }
   };
   // phase 2 of query tile jt (its dS^T tiles complete in buffer jt & 1):
@@ -643,8 +691,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 #pragma unroll
     for (int k8 = 0; k8 < 4 * KPW; k8++) {
       const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
-      const bf16x8 aop = lds_tr_op16(dtile, KP, 16 * qb, lane);
-      const bf16x8 bop = lds_tr_op16(sKr + k8 * TILE * KP, KP, 16 * cb, lane);
+      const bf16x8 aop = swz_tr_op16<true>(dtile, 16 * qb, lane);
+      const bf16x8 bop = swz_tr_op16<false>(sKr + k8 * TILE * KP, 16 * cb, lane);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc, 0, 0, 0);
     }
     // acc[i]: query jt*32 + 16qb + 4(lane>>4) + i, channel dq_c
@@ -665,10 +713,13 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
-      const T* d0 = sDT + ((b * 8 + ww) * KPW + t) * TILE * KP + l32 * KP + 16 * rg + 4 * g;
-      const T* d1 = sDT + ((b * 8 + 4 + ww) * KPW + t) * TILE * KP + l32 * KP + 16 * rg + 4 * g;
-      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(d0), x1 = *reinterpret_cast<const bf16x4*>(d0 + 8);
-      const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(d1), y1 = *reinterpret_cast<const bf16x4*>(d1 + 8);
+      const T* d0 = sDT + ((b * 8 + ww) * KPW + t) * TILE * KP;
+      const T* d1 = sDT + ((b * 8 + 4 + ww) * KPW + t) * TILE * KP;
+      const int c0 = 16 * rg + 4 * g;
+      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(d0 + swz8(l32, c0));
+      const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(d0 + swz8(l32, c0 + 8));
+      const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(d1 + swz8(l32, c0));
+      const bf16x4 y1 = *reinterpret_cast<const bf16x4*>(d1 + swz8(l32, c0 + 8));
       bf16x8 sum;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
