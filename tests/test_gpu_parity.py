@@ -245,3 +245,37 @@ def test_determinism_n768(device):
         again = run_gpu(xd)
         for key in first:
             assert torch.equal(first[key], again[key]), f"repeat {rep}: {key}"
+
+
+# --------------------------------------------------------------------------- other paths
+@pytest.mark.parametrize("n,dtype", [(300, torch.float32), (960, torch.bfloat16), (736, torch.float32)])
+def test_row_group_backward_sizes(device, n, dtype):
+    """Sizes past the per-row tile kernel's limit (fp32 n > 256, bf16 n > 768) take the
+    row-group backward; the largest accepted n of each dtype is included."""
+    assert n <= ta.max_n(dtype)
+    log(f"row-group backward n={n} dtype={dtype}")
+    xc = inputs.attn_inputs(n, 4, 32, dtype, seed=200 + n, bias_std=1.5)
+    xc["mask"] = inputs.random_mask(n, seed=n, p_keep=0.85, full_rows=(2,))
+    res = run_gpu(to_dev(xc, device))
+    rng = np.random.default_rng(n)
+    rows = sorted({0, 2, n // 2, n - 1, *rng.choice(n, 3, replace=False).tolist()})
+    qsel = sorted({0, 31, n - 1, *rng.choice(n, 3, replace=False).tolist()})
+    check_sampled(f"rows{n}", xc, res, TOL[dtype], False, rows, qsel)
+
+
+def test_autograd_function(device):
+    """torch.autograd through TriAttnFunction gives the C ABI's gradients."""
+    from triangle_attention_tri_amd.autograd import tri_attn
+    n = 40
+    log("autograd function")
+    xc = inputs.attn_inputs(n, 4, 32, torch.bfloat16, seed=41)
+    xc["mask"] = inputs.random_mask(n, seed=3, p_keep=0.8)
+    xd = to_dev(xc, device)
+    leaves = {k: xd[k].clone().requires_grad_(True) for k in ("q", "k", "v", "bias", "gate")}
+    out = tri_attn(leaves["q"], leaves["k"], leaves["v"], leaves["bias"], leaves["gate"], xd["mask"])
+    out.backward(xd["dout"])
+    torch.cuda.synchronize()
+    ref = oracle_rows(xc, list(range(n)), False)
+    assert_close("autograd out", out.detach().cpu(), ref["out"], 2e-2)
+    for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("bias", "dbias"), ("gate", "dgate")):
+        assert_close(f"autograd {key}", leaves[name].grad.cpu(), ref[key], 2e-2)
