@@ -128,7 +128,8 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     // bf16 sums the dS tiles of row pairs before storing them
     L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + 1) / 2 : n_rows;
     L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);
-    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * n_rows * h * n * C * es : 0));
+    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * dq_part_rows(n_rows) * h *
+                                                        dq_part_queries(n) * C * es : 0));
     L.total = align256(L.trash + BWD_TRASH_BYTES);
     return L;
   }

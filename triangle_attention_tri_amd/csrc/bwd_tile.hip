@@ -225,7 +225,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
     }
     for (int e = tid; e < n * C; e += 256) {
       const int jj = e / C, c = e % C;
-      if (a.nsplit > 1) reinterpret_cast<T*>(a.dq_part)[((long long)split * G.n_rows * G.H * n + irow + jj) * C + c] = from_f<T>(0.0f);
+      if (a.nsplit > 1) reinterpret_cast<T*>(a.dq_part)[dq_part_off(G, split, row, h, jj) + c] = from_f<T>(0.0f);
       else a.dq[row * G.qkv_row + headq + jj * G.qkv_pos + c] = from_f<T>(0.0f);
     }
     return;
@@ -398,7 +398,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
       const bool jv = jj < n;
       if (a.nsplit > 1) {
         // partial of this key range, rounded once to T (summed in fp32 by dq_sum_kernel)
-        T* dst = jv ? reinterpret_cast<T*>(a.dq_part) + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + c0
+        T* dst = jv ? reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, jj) + c0
                     : reinterpret_cast<T*>(dq_trash);
         if constexpr (sizeof(T) == 2)
           *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)sum[0], (bf16)sum[1], (bf16)sum[2], (bf16)sum[3]};
@@ -543,7 +543,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile addresses stay scalar
   const int rg = w >> 2, ww = w & 3;                       // row of the pair, wave within the row
   const int npairs = (G.n_rows + 1) / 2;
   const int item = xcd_item(blockIdx.x, a.nsplit * npairs * G.H);
@@ -591,45 +592,48 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   for (int t = 0; t < KPW; t++) kfull = kfull && kbits[t] == 0xffffffffu;
   kfull = __builtin_amdgcn_readfirstlane(kfull ? 1 : 0) != 0;
 
-  // staging: one 16-byte piece of the two rows' Q / dA tiles per thread, and
-  // (every thread, duplicates hitting the cache) four lse / D values
-  const int q_row = tid >> 8, q_which = (tid >> 7) & 1, q_jr = (tid >> 2) & 31, q_ch = tid & 3;
+  // staging: per thread, one 16-byte piece of a Q (q_which 0) or dA (1) tile
+  // row of one of the two rows, and that query's lse (q_which 0) or D (1)
+  const int q_row = w >> 2, q_which = (w >> 1) & 1, q_jr = (tid >> 2) & 31, q_ch = tid & 3;
   const int q_rowc = min(2 * pr + q_row, G.n_rows - 1);
   const T* q_base = q_which ? a.dA + ((long long)q_rowc * G.H + h) * n * C : a.q + q_rowc * G.qkv_row + headq;
   const long long q_pos = q_which ? C : G.qkv_pos;
-  const int l_idx = tid & 31, l_row = l_idx >> 4, l_which = (l_idx >> 3) & 1, l_j = 4 * (l_idx & 7);
-  const float* l_src = (l_which ? a.Dsum : a.lse) + ((long long)min(2 * pr + l_row, G.n_rows - 1) * G.H + h) * n;
+  const float* l_src = (q_which ? a.Dsum : a.lse) + ((long long)q_rowc * G.H + h) * n;
   V16 qpre;
-  f32x4 ldpre;
+  float lpre;
   auto issue_q = [&](int jt) __attribute__((always_inline)) {
-    qpre = reinterpret_cast<const V16*>(q_base + min(jt * TILE + q_jr, n - 1) * q_pos)[q_ch];
-#pragma unroll
-    for (int t = 0; t < 4; t++) ldpre[t] = l_src[min(jt * TILE + l_j + t, n - 1)];
+    const int jj = min(jt * TILE + q_jr, n - 1);
+    qpre = reinterpret_cast<const V16*>(q_base + jj * q_pos)[q_ch];
+    lpre = l_src[jj];
   };
   auto stash_q = [&](int buf, int jt) __attribute__((always_inline)) {
     *reinterpret_cast<V16*>(sQ + ((buf * 2 + q_row) * 2 + q_which) * TILE * KP + swz16(q_jr, q_ch * 8)) = qpre;
-    if (tid < 32) {
-      const int j0 = jt * TILE + l_j;
-      f32x4 v;
-#pragma unroll
-      for (int t = 0; t < 4; t++) v[t] = l_which == 0 ? (j0 + t < n ? ldpre[t] * LOG2E : POS_INF) : -ldpre[t];
-      *reinterpret_cast<f32x4*>(sLD + ((buf * 2 + l_row) * 2 + l_which) * TILE + l_j) = v;
-    }
+    if (q_ch == 0)
+      sLD[((buf * 2 + q_row) * 2 + q_which) * TILE + q_jr] =
+          q_which == 0 ? (jt * TILE + q_jr < n ? lpre * LOG2E : POS_INF) : -lpre;
   };
 
-  const float* bias_h = a.bias_prep + (long long)h * nt * nt * 1024 + lane * 16;
-  const float* bias_zero = a.bias_prep + (long long)G.H * nt * nt * 1024 + lane * 16;
+  // tile addresses: a workgroup-uniform tile base plus this lane's 16 values
+  const uint32_t lane16 = (uint32_t)lane * 16u;
   auto bias_ptr = [&](int jt, int ktl) __attribute__((always_inline)) {
-    return (jt < nt && ktl < nkt) ? bias_h + ((long long)jt * nt + kt0 + ktl) * 1024 : bias_zero;
+    // past the key range or the last query tile: the zero tile after the heads' tiles
+    const long long tile = (jt < nt && ktl < nkt) ? ((long long)h * nt + jt) * nt + kt0 + ktl : (long long)G.H * nt * nt;
+    return a.bias_prep + tile * 1024 + lane16;
   };
-  T* slab_row = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024 + lane * 16 + 8 * rg;
-  T* slab_trash = reinterpret_cast<T*>(a.trash) + lane * 16;
-  float* dq_trash = a.trash + 1024 + tid;
-  // this wave's dQ block: queries 16 qb.., channels 16 cb..
+  T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024 + 8 * rg;
+  // this wave's dQ block (transposed MFMA output): query 16 qb + (lane & 15),
+  // channels dq_c .. dq_c + 3.  The partials are padded (rows to even, queries
+  // to whole tiles), so every lane stores there; the final dQ (one key range)
+  // sends the lanes past the row's end to the trash area.
   const int qb = ww >> 1, cb = ww & 1;
-  const int dq_c = 16 * cb + (lane & 15);
+  const int dq_c = 16 * cb + 4 * (lane >> 4);
+  T* dq_part_row = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 0) + dq_c;
+  T* dq_trash = reinterpret_cast<T*>(a.trash + 1024) + 4 * tid;
 
-  f32x16 bnext;
+  // bias tiles prefetched one key tile ahead into two register sets: key tile t
+  // reads set t and loads the next tile into set (t + 1) % KPW, so no set is
+  // copied from one iteration to the next
+  f32x16 bpf[KPW];
   // phase 1 of query tile jt: per key tile, S and P recomputed once; dV, dK and
   // the dS^T tile (buffer jt & 1)
   auto phase1 = [&](int jt) __attribute__((always_inline)) {
@@ -646,8 +650,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
-      const f32x16 bias = bnext;
-      bnext = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, ww));
+      const f32x16 bias = bpf[t];
+      bpf[(t + 1) % KPW] = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, ww));
       const Op<T> kb = swz_c_op(sKr + ktl * TILE * KP, l32, g);
       const f32x16 s = mma32(qa, kb, bias);
       f32x16 p;
@@ -693,22 +697,18 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
       const bf16x8 aop = swz_tr_op16<true>(dtile, 16 * qb, lane);
       const bf16x8 bop = swz_tr_op16<false>(sKr + k8 * TILE * KP, 16 * cb, lane);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop, aop, acc, 0, 0, 0);  // (dS K)^T block
     }
-    // acc[i]: query jt*32 + 16qb + 4(lane>>4) + i, channel dq_c
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int jj = jt * TILE + 16 * qb + 4 * (lane >> 4) + i;
-      const bool ok = rvalid && jj < n;
-      if (a.nsplit > 1) {
-        // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
-        T* dst = ok ? reinterpret_cast<T*>(a.dq_part) + ((long long)split * G.n_rows * G.H * n + irow + jj) * C + dq_c
-                    : reinterpret_cast<T*>(dq_trash);
-        *dst = (bf16)acc[i];
-      } else {
-        T* dst = ok ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : reinterpret_cast<T*>(dq_trash);
-        *dst = (bf16)(acc[i] * INV_SQRT_C);
-      }
+    // acc[i]: channel dq_c + i of query jj
+    const int jj = jt * TILE + 16 * qb + (lane & 15);
+    if (a.nsplit > 1) {
+      // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
+      *reinterpret_cast<bf16x4*>(dq_part_row + (long long)jj * C) =
+          (bf16x4){(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
+    } else {
+      T* dst = rvalid && jj < n ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : dq_trash;
+      *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(acc[0] * INV_SQRT_C), (bf16)(acc[1] * INV_SQRT_C),
+                                                 (bf16)(acc[2] * INV_SQRT_C), (bf16)(acc[3] * INV_SQRT_C)};
     }
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
@@ -726,14 +726,14 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
         sum[e] = (bf16)((float)x0[e] + (float)y0[e]);
         sum[4 + e] = (bf16)((float)x1[e] + (float)y1[e]);
       }
-      T* dst = ktl < nkt ? slab_row + (jt * nt + kt0 + ktl) * 1024 : slab_trash;
+      T* dst = (ktl < nkt ? slab_pair + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) + lane16;
       *reinterpret_cast<bf16x8*>(dst) = sum;
     }
   };
 
   issue_q(0);
   stash_q(0, 0);
-  bnext = load_tile16<T>(bias_ptr(0, ww));
+  bpf[0] = load_tile16<T>(bias_ptr(0, ww));
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
   issue_q(1);
@@ -791,25 +791,25 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 template <typename T>
 __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
   const Geo& G = a.geo;
-  const long long per_split = (long long)G.n_rows * G.H * G.n * C;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t * 4 >= per_split) return;
+  if (t * 4 >= (long long)G.n_rows * G.H * G.n * C) return;
   const long long e = t * 4;
-  const T* part = reinterpret_cast<const T*>(a.dq_part);
-  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int sp = 0; sp < a.nsplit; sp++) {
-    if constexpr (sizeof(T) == 2) {
-      const bf16x4 x = *reinterpret_cast<const bf16x4*>(part + sp * per_split + e);
-      s[0] += (float)x[0]; s[1] += (float)x[1]; s[2] += (float)x[2]; s[3] += (float)x[3];
-    } else {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * per_split + e);
-      s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
-    }
-  }
   const int c0 = (int)(e % C);
   const int jj = (int)((e / C) % G.n);
   const int h = (int)((e / ((long long)C * G.n)) % G.H);
   const int row = (int)(e / ((long long)C * G.n * G.H));
+  const long long per_split = dq_part_rows(G.n_rows) * G.H * dq_part_queries(G.n) * C;
+  const T* part = reinterpret_cast<const T*>(a.dq_part) + dq_part_off(G, 0, row, h, jj) + c0;
+  f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sp = 0; sp < a.nsplit; sp++) {
+    if constexpr (sizeof(T) == 2) {
+      const bf16x4 x = *reinterpret_cast<const bf16x4*>(part + sp * per_split);
+      s[0] += (float)x[0]; s[1] += (float)x[1]; s[2] += (float)x[2]; s[3] += (float)x[3];
+    } else {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * per_split);
+      s[0] += x[0]; s[1] += x[1]; s[2] += x[2]; s[3] += x[3];
+    }
+  }
   T* dst = a.dq + row * G.qkv_row + (long long)h * G.n * C + jj * G.qkv_pos + c0;
   if constexpr (sizeof(T) == 2)
     *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(s[0] * INV_SQRT_C), (bf16)(s[1] * INV_SQRT_C),

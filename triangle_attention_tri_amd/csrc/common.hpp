@@ -270,6 +270,16 @@ template <typename T> struct FwdArgs {
 
 constexpr int BWD_TRASH_BYTES = 8192;
 
+// dQ partials of the key ranges: [range][row][h][query][c], with the row count
+// rounded up to even and the query count up to whole 32-query tiles, so that a
+// two-row workgroup stores every lane of a tile without a bounds select (the
+// padding is written, never read).
+__host__ __device__ inline long long dq_part_rows(int n_rows) { return n_rows + (n_rows & 1); }
+__host__ __device__ inline long long dq_part_queries(int n) { return (long long)((n + TILE - 1) / TILE) * TILE; }
+__device__ __forceinline__ long long dq_part_off(const Geo& G, int split, int row, int h, int jj) {
+  return (((split * dq_part_rows(G.n_rows) + row) * G.H + h) * dq_part_queries(G.n) + jj) * C;
+}
+
 template <typename T> struct BwdArgs {
   Geo geo;
   const T *q, *k, *v, *bias, *gate, *attn, *dout;
