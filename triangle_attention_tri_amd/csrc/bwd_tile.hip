@@ -520,6 +520,22 @@ __device__ __forceinline__ bf16x8 swz_tr_op16(const bf16* tile, int col0, int la
   const bf16x4 hi = lds_read_tr(tile + (S8 ? swz8(r + 4, c) : swz16(r + 4, c)));
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+// (x.lo + y.lo, x.hi + y.hi) of two packed bf16 pairs: each sum is one
+// v_dot2_f32_bf16 of x against (1, 0) or (0, 1) accumulating y's half widened
+// to fp32, rounded once to bf16.  The (1, 0) pair is held in an SGPR: as an
+// inline constant of the 32-bit dot2c form it would be read as fp32 1.0,
+// i.e. the pair (0, 1).
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t x, uint32_t y) {
+  uint32_t lo_one;
+  asm("s_mov_b32 %0, 0x3f80" : "=s"(lo_one));
+  const bf16x2 one_hi = {(bf16)0.0f, (bf16)1.0f};
+  const bf16x2 xv = __builtin_bit_cast(bf16x2, x);
+  const float s0 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, lo_one), __uint_as_float(y << 16), false);
+  const float s1 = __builtin_amdgcn_fdot2_f32_bf16(xv, one_hi, __uint_as_float(y & 0xffff0000u), false);
+  const bf16x2 r = {(bf16)s0, (bf16)s1};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 // dS (accumulator order) -> swz8 dS^T tile [key][query]
 __device__ __forceinline__ void swz_store_dst(bf16* tile, const Op<bf16>& o, int l32, int g) {
 #pragma unroll
@@ -716,18 +732,14 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       const T* d0 = sDT + ((b * 8 + ww) * KPW + t) * TILE * KP;
       const T* d1 = sDT + ((b * 8 + 4 + ww) * KPW + t) * TILE * KP;
       const int c0 = 16 * rg + 4 * g;
-      const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(d0 + swz8(l32, c0));
-      const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(d0 + swz8(l32, c0 + 8));
-      const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(d1 + swz8(l32, c0));
-      const bf16x4 y1 = *reinterpret_cast<const bf16x4*>(d1 + swz8(l32, c0 + 8));
-      bf16x8 sum;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        sum[e] = (bf16)((float)x0[e] + (float)y0[e]);
-        sum[4 + e] = (bf16)((float)x1[e] + (float)y1[e]);
-      }
+      const V8 x0 = *reinterpret_cast<const V8*>(d0 + swz8(l32, c0));
+      const V8 x1 = *reinterpret_cast<const V8*>(d0 + swz8(l32, c0 + 8));
+      const V8 y0 = *reinterpret_cast<const V8*>(d1 + swz8(l32, c0));
+      const V8 y1 = *reinterpret_cast<const V8*>(d1 + swz8(l32, c0 + 8));
+      const V16 sum = {add_bf16x2(x0[0], y0[0]), add_bf16x2(x0[1], y0[1]), add_bf16x2(x1[0], y1[0]),
+                       add_bf16x2(x1[1], y1[1])};
       T* dst = (ktl < nkt ? slab_pair + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) + lane16;
-      *reinterpret_cast<bf16x8*>(dst) = sum;
+      *reinterpret_cast<V16*>(dst) = sum;
     }
   };
 
@@ -739,25 +751,28 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   issue_q(1);
   phase1(0);
   stash_q(1, 1);
+  issue_q(2);
   __syncthreads();
   // Between two barriers each wave runs phase 1 of tile jt and phase 2 of tile
-  // jt - 1 (whose dS^T tiles sit in the other buffer), row group 0 in that
-  // order and row group 1 in the opposite order: the two waves that share a
-  // SIMD (one of each group) then run different instruction mixes at the same
-  // time instead of competing for the same units.
+  // jt - 1 (whose dS^T tiles sit in the other buffer): row group 0 in that
+  // order, row group 1 in the opposite order, so the two waves that share a
+  // SIMD (one of each group) run different instruction mixes at the same time
+  // instead of competing for the same units.  Both groups run one loop text,
+  // phase 1 (tile jt) then phase 2: group 0 takes phase 2 of tile jt - 1 before
+  // its barrier, group 1 takes its barrier first and then phase 2 of tile jt.
+  // One text keeps every accumulator in the same registers on both groups.
+  if (rg == 1) phase2(0);
+  // The staging registers are stored to LDS right after phase 1 and reloaded
+  // with the tile after next at once: each load has a whole iteration to land.
   for (int jt = 1; jt < nt; jt++) {
-    issue_q(jt + 1);  // clamped rows: the last iteration reloads the last tile, never used
-    if (rg == 0) {
-      phase1(jt);
-      phase2(jt - 1);
-    } else {
-      phase2(jt - 1);
-      phase1(jt);
-    }
+    phase1(jt);
     stash_q((jt + 1) & 1, jt + 1);
-    __syncthreads();
+    issue_q(jt + 2);  // clamped rows: past the last tile it reloads the last one, never used
+    if (rg == 1) __syncthreads();
+    phase2(jt - 1 + rg);
+    if (rg == 0) __syncthreads();
   }
-  phase2(nt - 1);
+  if (rg == 0) phase2(nt - 1);
 
   // dK and dV of this wave's key tiles (a fully masked row: dV = mean of dA, dK = 0)
   if (!rvalid) return;

@@ -166,6 +166,7 @@ __device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g
 // 16-byte vector used for staging copies (a native vector type, so it always
 // lives in registers)
 typedef uint32_t V16 __attribute__((ext_vector_type(4)));
+typedef uint32_t V8 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Operands read from row-major LDS tiles (32 rows, `pitch` elements per row).
