@@ -124,7 +124,8 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     L.rows = 1;
     L.nsplit = pick_nsplit(dtype, n);
     L.bias_prep = after_d;
-    L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * sizeof(float));
+    // prepared bias: fp16 for bf16 runs, fp32 for fp32 runs (plus one zero tile)
+    L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * (dtype == TRI_ATTN_BF16 ? 2 : 4));
     // bf16 sums the dS tiles of row pairs before storing them
     L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + 1) / 2 : n_rows;
     L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);

@@ -110,34 +110,48 @@ __global__ __launch_bounds__(256) void bwd_pre_vec_kernel(BwdArgs<T> a) {
 }
 
 // bias prep for the backward tile orientation (lane = key):
-// out[h][jt][kt][lane][r] = sqrt(c) * bias(j = jt*32 + mrow(lane>>5, r), k = kt*32 + (lane & 31))
-template <typename T>
-__global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias, float* out) {
+// out[h][jt][kt][lane][r] = sqrt(c) * bias(j = jt*32 + mrow(lane>>5, r), k = kt*32 + (lane & 31)),
+// stored as B: fp32 for fp32 runs; fp16 for bf16 runs, whose main kernel then
+// moves half the bytes per tile.  fp16 keeps 11 significant bits, so the scaled
+// bias is off by at most 2^-12 of itself (2^-12 |b| in logit units, four times
+// finer than the bf16 input's own spacing); it saturates at +-65504, i.e. for
+// |b| beyond 65504 / sqrt(c) ~ 11580.
+template <typename T, typename B>
+__global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias, B* out) {
   const int nt = (G.n + TILE - 1) / TILE;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)G.H * nt * nt * 64;
   if (t >= total + 64) return;
+  float v[16];
   if (t >= total) {  // the zero tile used by rows whose keys are all masked
+#pragma unroll
+    for (int r = 0; r < 16; r++) v[r] = 0.0f;
+  } else {
+    const int lane = (int)(t & 63);
+    const long long tile = t >> 6;
+    const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
+    const int k = kt * TILE + (lane & 31), g = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int j = jt * TILE + mrow(g, r);
+      v[r] = (j < G.n && k < G.n) ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C
+                                  : 0.0f;
+    }
+  }
+  if constexpr (sizeof(B) == 4) {
     f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
 #pragma unroll
-    for (int q = 0; q < 4; q++) o[q] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
-    return;
-  }
-  const int lane = (int)(t & 63);
-  const long long tile = t >> 6;
-  const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
-  const int k = kt * TILE + (lane & 31), g = lane >> 5;
-  f32x4 v[4];
+    for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  } else {
+    f16x8* o = reinterpret_cast<f16x8*>(out + t * 16);
 #pragma unroll
-  for (int r = 0; r < 16; r++) {
-    const int j = jt * TILE + mrow(g, r);
-    v[r >> 2][r & 3] = (j < G.n && k < G.n)
-                           ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C
-                           : 0.0f;
-  }
-  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+    for (int q = 0; q < 2; q++) {
+      f16x8 x;
 #pragma unroll
-  for (int q = 0; q < 4; q++) o[q] = v[q];
+      for (int e = 0; e < 8; e++) x[e] = (_Float16)fminf(fmaxf(v[8 * q + e], -65504.0f), 65504.0f);
+      o[q] = x;
+    }
+  }
 }
 
 template <typename T>
@@ -520,6 +534,18 @@ __device__ __forceinline__ bf16x8 swz_tr_op16(const bf16* tile, int col0, int la
   const bf16x4 hi = lds_read_tr(tile + (S8 ? swz8(r + 4, c) : swz16(r + 4, c)));
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
+// one lane's 16 fp16 bias values (two 16-byte loads), widened to fp32
+__device__ __forceinline__ f32x16 load_tile16_h(const _Float16* p) {
+  const f16x8 x = reinterpret_cast<const f16x8*>(p)[0], y = reinterpret_cast<const f16x8*>(p)[1];
+  f32x16 v;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    v[e] = (float)x[e];
+    v[8 + e] = (float)y[e];
+  }
+  return v;
+}
+
 // (x.lo + y.lo, x.hi + y.hi) of two packed bf16 pairs: each sum is one
 // v_dot2_f32_bf16 of x against (1, 0) or (0, 1) accumulating y's half widened
 // to fp32, rounded once to bf16.  The (1, 0) pair is held in an SGPR: as an
@@ -634,7 +660,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   auto bias_ptr = [&](int jt, int ktl) __attribute__((always_inline)) {
     // past the key range or the last query tile: the zero tile after the heads' tiles
     const long long tile = (jt < nt && ktl < nkt) ? ((long long)h * nt + jt) * nt + kt0 + ktl : (long long)G.H * nt * nt;
-    return a.bias_prep + tile * 1024 + lane16;
+    return reinterpret_cast<const _Float16*>(a.bias_prep) + tile * 1024 + lane16;
   };
   T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024 + 8 * rg;
   // this wave's dQ block (transposed MFMA output): query 16 qb + (lane & 15),
@@ -646,9 +672,9 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   T* dq_part_row = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 0) + dq_c;
   T* dq_trash = reinterpret_cast<T*>(a.trash + 1024) + 4 * tid;
 
-  // bias tiles prefetched one key tile ahead into two register sets: key tile t
-  // reads set t and loads the next tile into set (t + 1) % KPW, so no set is
-  // copied from one iteration to the next
+  // bias tiles: one register set per key tile of the wave, reloaded with the
+  // next query tile's tile as soon as the logit MFMA has taken it as its
+  // accumulator input, so every load has a whole iteration to land
   f32x16 bpf[KPW];
   // phase 1 of query tile jt: per key tile, S and P recomputed once; dV, dK and
   // the dS^T tile (buffer jt & 1)
@@ -666,10 +692,9 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       const int ktl = t * 4 + ww;
-      const f32x16 bias = bpf[t];
-      bpf[(t + 1) % KPW] = load_tile16<T>(t + 1 < KPW ? bias_ptr(jt, ktl + 4) : bias_ptr(jt + 1, ww));
       const Op<T> kb = swz_c_op(sKr + ktl * TILE * KP, l32, g);
-      const f32x16 s = mma32(qa, kb, bias);
+      const f32x16 s = mma32(qa, kb, bpf[t]);
+      bpf[t] = load_tile16_h(bias_ptr(jt + 1, ktl));
       f32x16 p;
 #pragma unroll
       for (int s4 = 0; s4 < 4; s4++) {
@@ -745,7 +770,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
 
   issue_q(0);
   stash_q(0, 0);
-  bpf[0] = load_tile16<T>(bias_ptr(0, ww));
+#pragma unroll
+  for (int t = 0; t < KPW; t++) bpf[t] = load_tile16_h(bias_ptr(0, t * 4 + ww));
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
   issue_q(1);
@@ -818,7 +844,7 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
   f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int sp = 0; sp < a.nsplit; sp++) {
     if constexpr (sizeof(T) == 2) {
-      const bf16x4 x = *reinterpret_cast<const bf16x4*>(part + sp * per_split);
+      const bf16x4 x = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(part + sp * per_split));
       s[0] += (float)x[0]; s[1] += (float)x[1]; s[2] += (float)x[2]; s[3] += (float)x[3];
     } else {
       const f32x4 x = *reinterpret_cast<const f32x4*>(part + sp * per_split);
@@ -839,7 +865,7 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
 template <typename T>
 __device__ __forceinline__ void load_half_tile(const T* p, float (&v)[8]);
 template <> __device__ __forceinline__ void load_half_tile<bf16>(const bf16* p, float (&v)[8]) {
-  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+  const bf16x8 x = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));  // read once: streaming
 #pragma unroll
   for (int i = 0; i < 8; i++) v[i] = (float)x[i];
 }
@@ -901,8 +927,8 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
-  hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
-                     a.bias, a.bias_prep);
+  hipLaunchKernelGGL((bwd_bias_prep_kernel<T, float>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
+                     G, a.bias, a.bias_prep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;
@@ -942,8 +968,8 @@ hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* e
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
-  hipLaunchKernelGGL((bwd_bias_prep_kernel<bf16>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
-                     a.bias, a.bias_prep);
+  hipLaunchKernelGGL((bwd_bias_prep_kernel<bf16, _Float16>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256),
+                     0, st, G, a.bias, reinterpret_cast<_Float16*>(a.bias_prep));
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;

@@ -167,6 +167,7 @@ __device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g
 // lives in registers)
 typedef uint32_t V16 __attribute__((ext_vector_type(4)));
 typedef uint32_t V8 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // Operands read from row-major LDS tiles (32 rows, `pitch` elements per row).
@@ -292,8 +293,9 @@ template <typename T> struct BwdArgs {
   float* slabs;    // workspace [groups][H][n][n] dbias partial per row group (row-group kernel)
   int groups;
   float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order, + one zero tile
+                     // (fp32; the bf16 two-row kernel reads it as fp16)
   T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
-  void* dq_part;     // workspace [nsplit][n_rows][H][n][C] dQ partial per key split (nsplit > 1), in T
+  void* dq_part;     // workspace [nsplit][rows, even][H][n, whole tiles][C] dQ partial per key split (nsplit > 1), in T
   float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
                      // the tile loop's memory instructions do not depend on branches
   int nsplit;        // key-range splits per row in the tile kernel
