@@ -534,17 +534,6 @@ __device__ __forceinline__ bf16x8 swz_tr_op16(const bf16* tile, int col0, int la
   const bf16x4 hi = lds_read_tr(tile + (S8 ? swz8(r + 4, c) : swz16(r + 4, c)));
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-// one lane's 16 fp16 bias values (two 16-byte loads), widened to fp32
-__device__ __forceinline__ f32x16 load_tile16_h(const _Float16* p) {
-  const f16x8 x = reinterpret_cast<const f16x8*>(p)[0], y = reinterpret_cast<const f16x8*>(p)[1];
-  f32x16 v;
-#pragma unroll
-  for (int e = 0; e < 8; e++) {
-    v[e] = (float)x[e];
-    v[8 + e] = (float)y[e];
-  }
-  return v;
-}
 
 // (x.lo + y.lo, x.hi + y.hi) of two packed bf16 pairs: each sum is one
 // v_dot2_f32_bf16 of x against (1, 0) or (0, 1) accumulating y's half widened

@@ -267,7 +267,7 @@ template <typename T> struct FwdArgs {
   const uint8_t* mask;
   T *out, *attn;
   float* lse;
-  float* bias_prep;  // workspace: sqrt(c)-scaled bias in per-lane tile order
+  float* bias_prep;  // workspace: sqrt(c)-scaled bias in per-lane tile order (fp32; fp16 for bf16 runs)
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;
@@ -315,6 +315,21 @@ __device__ __forceinline__ f32x16 load_tile16(const float* base) {
   }
   return v;
 }
+
+// one lane's 16 fp16 bias values (two 16-byte loads), widened to fp32
+__device__ __forceinline__ f32x16 load_tile16_h(const _Float16* p) {
+  const f16x8 x = reinterpret_cast<const f16x8*>(p)[0], y = reinterpret_cast<const f16x8*>(p)[1];
+  f32x16 v;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    v[e] = (float)x[e];
+    v[8 + e] = (float)y[e];
+  }
+  return v;
+}
+// the prepared-bias tile of a lane in its storage type, as fp32 registers
+__device__ __forceinline__ f32x16 load_bias_tile(const float* p) { return load_tile16<float>(p); }
+__device__ __forceinline__ f32x16 load_bias_tile(const _Float16* p) { return load_tile16_h(p); }
 
 // XCD-aware work order.  Workgroups are dispatched to the eight XCDs round
 // robin (workgroup b runs on XCD b % 8, each with its own L2).  This maps the

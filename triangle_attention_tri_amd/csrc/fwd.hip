@@ -25,6 +25,8 @@
 // The N^2 x N logit tensor never leaves the chip (MegaFold explainer,
 // EvoFlash-3D paragraph: the cubic interaction map is produced tile by tile in
 // fast on-chip memory and discarded).
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace tri {
@@ -35,8 +37,13 @@ constexpr float SUM_LIMIT = 4096.0f;  // a lane's tile sum above this moves the 
 
 // bias prep for the forward: out[h][jt][kt][lane][r] = sqrt(c) * bias(j, k) with
 // j = jt*32 + (lane & 31), k = kt*32 + mrow(lane >> 5, r); zero outside n.
+// Stored as B: fp32 for fp32 runs, fp16 for bf16 runs (half the bytes the main
+// loop reads; 11 significant bits, i.e. the scaled bias within 2^-12 of itself,
+// saturating at +-65504).
+template <typename T> using bias_store_t = typename std::conditional<sizeof(T) == 2, _Float16, float>::type;
+
 template <typename T>
-__global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias, float* out) {
+__global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias, bias_store_t<T>* out) {
   const int nt = (G.n + TILE - 1) / TILE;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one thread per (h, jt, kt, lane)
   const long long total = (long long)G.H * nt * nt * 64;
@@ -45,17 +52,26 @@ __global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias
   const long long tile = t >> 6;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
   const int j = jt * TILE + (lane & 31), g = lane >> 5;
-  f32x4 v[4];
+  float v[16];
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int k = kt * TILE + mrow(g, r);
-    v[r >> 2][r & 3] = (j < G.n && k < G.n)
-                           ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C
-                           : 0.0f;
+    v[r] = (j < G.n && k < G.n) ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C : 0.0f;
   }
-  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+  if constexpr (sizeof(T) == 4) {
+    f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
 #pragma unroll
-  for (int q = 0; q < 4; q++) o[q] = v[q];
+    for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  } else {
+    f16x8* o = reinterpret_cast<f16x8*>(out + t * 16);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      f16x8 x;
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = (_Float16)fminf(fmaxf(v[8 * q + e], -65504.0f), 65504.0f);
+      o[q] = x;
+    }
+  }
 }
 
 // Longest key axis whose per-tile mask words fit the LDS table below.
@@ -86,8 +102,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
   const bool jvalid = j < n;
   const long long headq = (long long)h * n * C;
   // bias tiles of this wave's query tile (a wave past the last query tile reads the last one, unused)
-  const f32x4* biasp = reinterpret_cast<const f32x4*>(a.bias_prep) +
-                       ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 4;
+  const bias_store_t<T>* biasp = reinterpret_cast<const bias_store_t<T>*>(a.bias_prep) +
+                                 ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 16;
 
   // key masks: one word per (row, key tile); keys past n are never kept
   for (int idx = w; idx < R * nt; idx += 4) {
@@ -135,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
     }
   };
   auto load_bias = [&](int kt) __attribute__((always_inline)) {
-    return load_tile16<T>(reinterpret_cast<const float*>(biasp + (long long)min(kt, nt - 1) * 64 * 4));
+    return load_bias_tile(biasp + (long long)min(kt, nt - 1) * 64 * 16);
   };
 
   // one key tile for all R rows
@@ -259,7 +275,7 @@ hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
   const int nt = (G.n + TILE - 1) / TILE;
   const long long prep_threads = (long long)G.H * nt * nt * 64;
   hipLaunchKernelGGL((fwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
-                     a.bias, a.bias_prep);
+                     a.bias, reinterpret_cast<bias_store_t<T>*>(a.bias_prep));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int blocks = ((G.n + 127) / 128) * ((G.n_rows + R - 1) / R) * G.H;
