@@ -154,18 +154,24 @@ __global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias
   }
 }
 
+// dS slab tiles (1024 values, accumulator order) are laid out [half][lane][8]:
+// lane l's values r = 8 * half .. + 7 at half * SLAB_HALF + 8 * l, so that a
+// wave storing one half writes 64 lanes x 8 values contiguously (whole cache
+// lines).  store_tile_op stores both halves of a lane from dst = tile + 8 * lane.
+constexpr int SLAB_HALF = 512;
 template <typename T>
 __device__ __forceinline__ void store_tile_op(T* dst, const Op<T>& o);
 template <>
 __device__ __forceinline__ void store_tile_op<bf16>(bf16* dst, const Op<bf16>& o) {
-  reinterpret_cast<bf16x8*>(dst)[0] = o.f[0];
-  reinterpret_cast<bf16x8*>(dst)[1] = o.f[1];
+  *reinterpret_cast<bf16x8*>(dst) = o.f[0];
+  *reinterpret_cast<bf16x8*>(dst + SLAB_HALF) = o.f[1];
 }
 template <>
 __device__ __forceinline__ void store_tile_op<float>(float* dst, const Op<float>& o) {
-  f32x4* d = reinterpret_cast<f32x4*>(dst);
 #pragma unroll
-  for (int q = 0; q < 4; q++) d[q] = (f32x4){o.f[4 * q], o.f[4 * q + 1], o.f[4 * q + 2], o.f[4 * q + 3]};
+  for (int q = 0; q < 4; q++)
+    *reinterpret_cast<f32x4*>(dst + (q >> 1) * SLAB_HALF + 4 * (q & 1)) =
+        (f32x4){o.f[4 * q], o.f[4 * q + 1], o.f[4 * q + 2], o.f[4 * q + 3]};
 }
 
 // dS (operand precision, accumulator order) -> per-wave LDS tile laid out [key][query]
@@ -222,7 +228,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
   const long long headq = (long long)h * n * C;
   const long long irow = ((long long)row * G.H + h) * n;
   const T* qrow = a.q + row * G.qkv_row + headq;
-  T* slab_row = a.tslab + ((long long)row * G.H + h) * nt * nt * 1024 + lane * 16;
+  T* slab_row = a.tslab + ((long long)row * G.H + h) * nt * nt * 1024 + lane * 8;
   if (!row_has_valid_key(a.mask, G, row, lane)) {
     // every key masked: P = 1/n everywhere, dS = 0
     for (int ktl = w; ktl < nkt; ktl += 4) {
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
   // one completion counter, and with a fixed sequence of memory instructions
   // per iteration the waits for prefetched data count exactly instead of
   // draining every outstanding store.
-  T* slab_trash = reinterpret_cast<T*>(a.trash) + lane * 16;
+  T* slab_trash = reinterpret_cast<T*>(a.trash) + lane * 8;
   float* dq_trash = a.trash + 1024 + tid * 4;
 
   issue_q(0);
@@ -651,7 +657,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const long long tile = (jt < nt && ktl < nkt) ? ((long long)h * nt + jt) * nt + kt0 + ktl : (long long)G.H * nt * nt;
     return reinterpret_cast<const _Float16*>(a.bias_prep) + tile * 1024 + lane16;
   };
-  T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024 + 8 * rg;
+  T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024;
   // this wave's dQ block (transposed MFMA output): query 16 qb + (lane & 15),
   // channels dq_c .. dq_c + 3.  The partials are padded (rows to even, queries
   // to whole tiles), so every lane stores there; the final dQ (one key range)
@@ -752,7 +758,8 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
       const V8 y1 = *reinterpret_cast<const V8*>(d1 + swz8(l32, c0 + 8));
       const V16 sum = {add_bf16x2(x0[0], y0[0]), add_bf16x2(x0[1], y0[1]), add_bf16x2(x1[0], y1[0]),
                        add_bf16x2(x1[1], y1[1])};
-      T* dst = (ktl < nkt ? slab_pair + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) + lane16;
+      T* dst = (ktl < nkt ? slab_pair + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) +
+               rg * SLAB_HALF + lane * 8;  // this wave's half of the tile: whole lines
       *reinterpret_cast<V16*>(dst) = sum;
     }
   };
@@ -871,8 +878,8 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per slab
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= per_row / 8) return;
-  const long long e0 = t * 8;  // first element: [h][jt][kt][lane][r0..r0+7]
-  const int r0 = (int)(e0 & 15), lane = (int)((e0 >> 4) & 63);
+  const long long e0 = t * 8;  // first element: [h][jt][kt][half][lane][8], r0 = 8 * half
+  const int r0 = (int)((e0 >> 9) & 1) * 8, lane = (int)((e0 >> 3) & 63);
   const long long tile = e0 >> 10;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
   float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
