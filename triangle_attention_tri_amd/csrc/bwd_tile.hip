@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
     }
     for (int e = tid; e < n * C; e += 256) {
       const int jj = e / C, c = e % C;
-      if (a.nsplit > 1) reinterpret_cast<T*>(a.dq_part)[dq_part_off(G, split, row, h, jj) + c] = from_f<T>(0.0f);
+      if (a.nsplit > 1) reinterpret_cast<T*>(a.dq_part)[dq_part_off(G, split, row, h, jj, c)] = from_f<T>(0.0f);
       else a.dq[row * G.qkv_row + headq + jj * G.qkv_pos + c] = from_f<T>(0.0f);
     }
     return;
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
       const bool jv = jj < n;
       if (a.nsplit > 1) {
         // partial of this key range, rounded once to T (summed in fp32 by dq_sum_kernel)
-        T* dst = jv ? reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, jj) + c0
+        T* dst = jv ? reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, jj, c0)
                     : reinterpret_cast<T*>(dq_trash);
         if constexpr (sizeof(T) == 2)
           *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)sum[0], (bf16)sum[1], (bf16)sum[2], (bf16)sum[3]};
@@ -660,11 +660,12 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024;
   // this wave's dQ block (transposed MFMA output): query 16 qb + (lane & 15),
   // channels dq_c .. dq_c + 3.  The partials are padded (rows to even, queries
-  // to whole tiles), so every lane stores there; the final dQ (one key range)
-  // sends the lanes past the row's end to the trash area.
+  // to whole tiles), so every lane stores there, the wave's block as 512
+  // contiguous bytes; the final dQ (one key range) sends the lanes past the
+  // row's end to the trash area.
   const int qb = ww >> 1, cb = ww & 1;
   const int dq_c = 16 * cb + 4 * (lane >> 4);
-  T* dq_part_row = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 0) + dq_c;
+  T* dq_part_blk = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 16 * qb, 16 * cb) + (lane & 15) * 16 + 4 * (lane >> 4);
   T* dq_trash = reinterpret_cast<T*>(a.trash + 1024) + 4 * tid;
 
   // bias tiles: one register set per key tile of the wave, reloaded with the
@@ -739,7 +740,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const int jj = jt * TILE + 16 * qb + (lane & 15);
     if (a.nsplit > 1) {
       // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
-      *reinterpret_cast<bf16x4*>(dq_part_row + (long long)jj * C) =
+      *reinterpret_cast<bf16x4*>(dq_part_blk + jt * 2 * 512) =
           (bf16x4){(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
     } else {
       T* dst = rvalid && jj < n ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : dq_trash;
@@ -836,7 +837,7 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
   const int h = (int)((e / ((long long)C * G.n)) % G.H);
   const int row = (int)(e / ((long long)C * G.n * G.H));
   const long long per_split = dq_part_rows(G.n_rows) * G.H * dq_part_queries(G.n) * C;
-  const T* part = reinterpret_cast<const T*>(a.dq_part) + dq_part_off(G, 0, row, h, jj) + c0;
+  const T* part = reinterpret_cast<const T*>(a.dq_part) + dq_part_off(G, 0, row, h, jj, c0);
   f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int sp = 0; sp < a.nsplit; sp++) {
     if constexpr (sizeof(T) == 2) {

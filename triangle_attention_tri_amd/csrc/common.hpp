@@ -272,14 +272,17 @@ template <typename T> struct FwdArgs {
 
 constexpr int BWD_TRASH_BYTES = 8192;
 
-// dQ partials of the key ranges: [range][row][h][query][c], with the row count
-// rounded up to even and the query count up to whole 32-query tiles, so that a
+// dQ partials of the key ranges: per (range, row, h) a block of whole 32-query
+// tiles, each [channel half][32 queries][16 channels], so that a wave's 16 x 16
+// block of a tile (16 queries, one channel half) is 512 contiguous bytes.  The
+// row count is rounded up to even and the query count up to whole tiles, so a
 // two-row workgroup stores every lane of a tile without a bounds select (the
 // padding is written, never read).
 __host__ __device__ inline long long dq_part_rows(int n_rows) { return n_rows + (n_rows & 1); }
 __host__ __device__ inline long long dq_part_queries(int n) { return (long long)((n + TILE - 1) / TILE) * TILE; }
-__device__ __forceinline__ long long dq_part_off(const Geo& G, int split, int row, int h, int jj) {
-  return (((split * dq_part_rows(G.n_rows) + row) * G.H + h) * dq_part_queries(G.n) + jj) * C;
+__device__ __forceinline__ long long dq_part_off(const Geo& G, int split, int row, int h, int jj, int c) {
+  return ((split * dq_part_rows(G.n_rows) + row) * G.H + h) * dq_part_queries(G.n) * C +
+         ((jj >> 5) * 2 + (c >> 4)) * 512 + (jj & 31) * 16 + (c & 15);
 }
 
 template <typename T> struct BwdArgs {
