@@ -53,7 +53,7 @@ template <typename T> struct TileSmem {
 // thread moves three 8-channel vectors in and two out with vector accesses.
 template <typename T> __device__ __forceinline__ void load8(const T* p, float (&f)[8]);
 template <> __device__ __forceinline__ void load8<bf16>(const bf16* p, float (&f)[8]) {
-  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+  const bf16x8 v = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));  // read once: streaming
 #pragma unroll
   for (int c = 0; c < 8; c++) f[c] = (float)v[c];
 }
