@@ -685,40 +685,54 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const Op<T> qt = swz_tr_op_m(tq, lane);
     const Op<T> dat = swz_tr_op_m(tda, lane);
     T* wdt = sDT + ((b * 8 + w) * KPW) * TILE * KP;
+    f32x16 dng;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + 8 * s4);
+#pragma unroll
+      for (int q = 0; q < 4; q++) dng[4 * s4 + q] = d4[q];
+    }
+    // Software pipeline over the wave's key tiles: the logits and dP - D of
+    // key tile t + 1 are issued before the exponentials of tile t (and dP - D
+    // of tile 0 with its logits), so the matrix pipe runs them while the
+    // VALU works.  The scheduling barrier keeps that order.
+    f32x16 s_cur = mma32(qa, swz_c_op(sKr + ww * TILE * KP, l32, g), bpf[0]);
+    bpf[0] = load_tile16_h(bias_ptr(jt + 1, ww));
+    f32x16 dp_cur = mma32(daa, vb[0], dng);
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
-      const int ktl = t * 4 + ww;
-      const Op<T> kb = swz_c_op(sKr + ktl * TILE * KP, l32, g);
-      const f32x16 s = mma32(qa, kb, bpf[t]);
-      bpf[t] = load_tile16_h(bias_ptr(jt + 1, ktl));
+      f32x16 s_next, dp_next;
+      if (t + 1 < KPW) {
+        const int kn = (t + 1) * 4 + ww;
+        s_next = mma32(qa, swz_c_op(sKr + kn * TILE * KP, l32, g), bpf[t + 1]);
+        bpf[t + 1] = load_tile16_h(bias_ptr(jt + 1, kn));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 p;
 #pragma unroll
       for (int s4 = 0; s4 < 4; s4++) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(tl + 8 * s4);
 #pragma unroll
-        for (int q = 0; q < 4; q++) p[4 * s4 + q] = fast_exp2(__builtin_fmaf(s[4 * s4 + q], SC, -l4[q]));
+        for (int q = 0; q < 4; q++) p[4 * s4 + q] = fast_exp2(__builtin_fmaf(s_cur[4 * s4 + q], SC, -l4[q]));
       }
       if (!kfull) {
         const bool kv = (kbits[t] >> l32) & 1u;
 #pragma unroll
         for (int r = 0; r < 16; r++) p[r] = kv ? p[r] : 0.0f;
       }
-      f32x16 dng;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; s4++) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(td + 8 * s4);
-#pragma unroll
-        for (int q = 0; q < 4; q++) dng[4 * s4 + q] = d4[q];
-      }
-      const f32x16 dp = mma32(daa, vb[t], dng);
       f32x16 ds;
 #pragma unroll
-      for (int r = 0; r < 16; r++) ds[r] = p[r] * dp[r];
+      for (int r = 0; r < 16; r++) ds[r] = p[r] * dp_cur[r];
+      if (t + 1 < KPW) dp_next = mma32(daa, vb[t + 1], dng);
       const Op<T> pb = acc_op<T>(p);
       const Op<T> dsb = acc_op<T>(ds);
       dvt[t] = mma32(dat, pb, dvt[t]);
       dkt[t] = mma32(qt, dsb, dkt[t]);
       swz_store_dst(wdt + t * TILE * KP, dsb, l32, g);
+      if (t + 1 < KPW) {
+        s_cur = s_next;
+        dp_cur = dp_next;
+      }
     }
   };
   // phase 2 of query tile jt (its dS^T tiles complete in buffer jt & 1):
