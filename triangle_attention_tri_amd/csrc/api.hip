@@ -11,8 +11,8 @@ template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_
 template <typename T, int R> size_t bwd_main_smem(int n);
 template <typename T, int KPW> hipError_t launch_bwd_tile(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T> size_t tile_smem(int kpw);
-template <int KPW> hipError_t launch_bwd_pair(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-size_t pair_smem(int kpw);
+template <int KPW> hipError_t launch_bwd_group(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+size_t group_smem(int kpw);
 }  // namespace tri
 
 using namespace tri;
@@ -87,23 +87,25 @@ Geo make_geo(int n_rows, int n, int h, int ending) {
   return g;
 }
 
-// Key ranges per row and key tiles per wave of the per-row backward kernel
-// (kpw 0: use the row-group kernel).  bf16 rows are split into ranges of at
-// most eight 32-key tiles, so each of the four waves holds at most two key
-// tiles and two workgroups fit on a CU (measured at n = 768: three ranges of
-// eight tiles 1.87 ms, two ranges of twelve 2.21 ms for the main kernel).
+// Key ranges per row and key tiles per wave of the tiled backward kernels
+// (kpw 0: use the fallback rows kernel).  fp32: one row per four-wave
+// workgroup, the whole key axis in one range.  bf16: BF16_GROUP_ROWS rows per
+// eight-wave workgroup, 8 / BF16_GROUP_ROWS waves per row, each holding at
+// most two key tiles, so a key range is at most 16 / BF16_GROUP_ROWS tiles.
+int waves_per_row(int dtype) { return dtype == TRI_ATTN_BF16 ? 8 / BF16_GROUP_ROWS : 4; }
 int pick_nsplit(int dtype, int n) {
   const int nt = (n + TILE - 1) / TILE;
   if (dtype != TRI_ATTN_BF16) return 1;
-  return (nt + 7) / 8;
+  const int tpr = 2 * waves_per_row(dtype);
+  return (nt + tpr - 1) / tpr;
 }
 int pick_kpw(int dtype, int n) {
-  const int nt = (n + TILE - 1) / TILE, ns = pick_nsplit(dtype, n);
+  const int nt = (n + TILE - 1) / TILE, ns = pick_nsplit(dtype, n), wpr = waves_per_row(dtype);
   if (ns < 1) return 0;
-  const int tps = (nt + ns - 1) / ns, kpw = (tps + 3) / 4;
+  const int tps = (nt + ns - 1) / ns, kpw = (tps + wpr - 1) / wpr;
   const int max_kpw = 2;
   if (kpw > max_kpw) return 0;
-  const size_t smem = dtype == TRI_ATTN_BF16 ? pair_smem(kpw) : tile_smem<float>(kpw);
+  const size_t smem = dtype == TRI_ATTN_BF16 ? group_smem(kpw) : tile_smem<float>(kpw);
   return smem <= LDS_LIMIT ? kpw : 0;
 }
 
@@ -126,8 +128,8 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     L.bias_prep = after_d;
     // prepared bias: fp16 for bf16 runs, fp32 for fp32 runs (plus one zero tile)
     L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * (dtype == TRI_ATTN_BF16 ? 2 : 4));
-    // bf16 sums the dS tiles of row pairs before storing them
-    L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + 1) / 2 : n_rows;
+    // bf16 sums the dS tiles of each row group before storing them
+    L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS : n_rows;
     L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);
     L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * dq_part_rows(n_rows) * h *
                                                         dq_part_queries(n) * C * es : 0));
@@ -184,11 +186,12 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   hipError_t e;
   if (L.kpw > 0) {
     a.slab_rows = L.slab_rows;
+    a.slab_e = sizeof(T) == 2 ? 16 / BF16_GROUP_ROWS : 8;
     if constexpr (sizeof(T) == 2) {
-      // bf16: two rows per workgroup (pair-summed dS slabs)
+      // bf16: BF16_GROUP_ROWS rows per workgroup (group-summed dS slabs)
       switch (L.kpw) {
-        case 1: e = launch_bwd_pair<1>(a, st, ev); break;
-        case 2: e = launch_bwd_pair<2>(a, st, ev); break;
+        case 1: e = launch_bwd_group<1>(a, st, ev); break;
+        case 2: e = launch_bwd_group<2>(a, st, ev); break;
         default: return TRI_ATTN_EUNSUPPORTED;
       }
     } else {

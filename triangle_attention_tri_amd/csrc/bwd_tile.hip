@@ -464,27 +464,30 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 2 : 1)) void bwd_tile_kernel
 }
 
 // ---------------------------------------------------------------------------
-// Two-row variant (bf16): one workgroup of eight waves per (row pair, head,
-// key range).  Waves 0-3 take row i, waves 4-7 row i + 1, with the same key
-// tiles in the same positions, so that
-//  * the pair-bias gradient slab holds dS_i + dS_{i+1}: half the slab traffic
-//    and half the rows for the reduction to sum (each wave of a pair stores
-//    one half of every tile it shares with its partner, adding the two waves'
-//    rounded dS in row order);
+// Row-group variant (bf16): one workgroup of eight waves per (group of NR rows,
+// head, key range).  Each row has 8 / NR waves; each wave owns KPW key tiles of
+// its row, and every row of the group has the same key tiles in the same
+// positions, so that
+//  * the pair-bias gradient slab holds the sum of the group's NR dS tiles:
+//    1/NR of the per-row slab traffic and of the rows the reduction sums.
+//    The NR waves that share a key tile each store one of its NR parts, adding
+//    the NR rounded dS values in row order;
 //  * dQ needs no cross-wave sum: after the one barrier of an iteration each
-//    wave forms a 16 x 16 block of its row's dQ tile over all the key tiles
-//    with 16x16x32 MFMAs, reading the dS^T tiles of its row's four waves
-//    (double-buffered, so the next iteration's phase 1 may overwrite the
-//    other buffer without a second barrier).
-// A row past the last one (odd row count) or with every key masked runs the
-// tile loop with an all-zero key mask (P = dS = 0), so every wave issues the
-// same instruction sequence; its outputs are written after the loop.
-struct PairSmem {
+//    wave forms its 16 x 16 blocks of its row's dQ tile over all the key
+//    tiles of the range with 16x16x32 MFMAs, reading the dS^T tiles of its
+//    row's waves (double-buffered, so the next iteration's phase 1 may
+//    overwrite the other buffer without a second barrier).
+// A row past the last one or with every key masked runs the tile loop with an
+// all-zero key mask (P = dS = 0), so every wave issues the same instruction
+// sequence; its outputs are written after the loop.
+template <int NR>
+struct GroupSmem {
   static constexpr int KP = TILE;                                      // unpadded rows, swizzled
+  static constexpr int WPR = 8 / NR;                                   // waves per row
   static constexpr size_t tile = 2 * TILE * KP;                        // one bf16 32 x 32 tile
-  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)2 * 4 * kpw * tile; }
-  static constexpr size_t qd_bytes = 2 * 2 * 2 * tile;                   // [buffer][row][Q, dA]
-  static constexpr size_t ld_bytes = 2 * 2 * 2 * TILE * sizeof(float);   // [buffer][row][lse, -D]
+  static constexpr __host__ __device__ size_t k_bytes(int kpw) { return (size_t)NR * WPR * kpw * tile; }
+  static constexpr size_t qd_bytes = (size_t)2 * NR * 2 * tile;                   // [buffer][row][Q, dA]
+  static constexpr size_t ld_bytes = (size_t)2 * NR * 2 * TILE * sizeof(float);   // [buffer][row][lse, -D]
   static constexpr __host__ __device__ size_t dt_bytes(int kpw) { return (size_t)2 * 8 * kpw * tile; }
   static constexpr __host__ __device__ size_t total(int kpw) {
     return k_bytes(kpw) + qd_bytes + ld_bytes + dt_bytes(kpw);
@@ -541,20 +544,27 @@ __device__ __forceinline__ bf16x8 swz_tr_op16(const bf16* tile, int col0, int la
   return (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// (x.lo + y.lo, x.hi + y.hi) of two packed bf16 pairs: each sum is one
-// v_dot2_f32_bf16 of x against (1, 0) or (0, 1) accumulating y's half widened
-// to fp32, rounded once to bf16.  The (1, 0) pair is held in an SGPR: as an
-// inline constant of the 32-bit dot2c form it would be read as fp32 1.0,
-// i.e. the pair (0, 1).
-__device__ __forceinline__ uint32_t add_bf16x2(uint32_t x, uint32_t y) {
+// Sum over the NR rows of a group of two packed bf16 values per row, each
+// sum in fp32 and rounded once to bf16, rows added in order: the running sum
+// starts as row 0's value plus row 1's and takes one v_dot2_f32_bf16 per
+// further row, which multiplies the row's pair by (1, 0) or (0, 1) and
+// accumulates.  The (1, 0) pair is held in an SGPR: as an inline constant of
+// the 32-bit dot2c form it would be read as fp32 1.0, i.e. the pair (0, 1).
+template <int NR>
+__device__ __forceinline__ uint32_t sum_rows_bf16x2(const uint32_t (&x)[NR]) {
   uint32_t lo_one;
   asm("s_mov_b32 %0, 0x3f80" : "=s"(lo_one));
-  const bf16x2 one_hi = {(bf16)0.0f, (bf16)1.0f};
-  const bf16x2 xv = __builtin_bit_cast(bf16x2, x);
-  const float s0 = __builtin_amdgcn_fdot2_f32_bf16(xv, __builtin_bit_cast(bf16x2, lo_one), __uint_as_float(y << 16), false);
-  const float s1 = __builtin_amdgcn_fdot2_f32_bf16(xv, one_hi, __uint_as_float(y & 0xffff0000u), false);
-  const bf16x2 r = {(bf16)s0, (bf16)s1};
-  return __builtin_bit_cast(uint32_t, r);
+  const bf16x2 one_lo = __builtin_bit_cast(bf16x2, lo_one), one_hi = {(bf16)0.0f, (bf16)1.0f};
+  float s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[1]), one_lo, __uint_as_float(x[0] << 16), false);
+  float s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[1]), one_hi,
+                                             __uint_as_float(x[0] & 0xffff0000u), false);
+#pragma unroll
+  for (int r = 2; r < NR; r++) {
+    s0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[r]), one_lo, s0, false);
+    s1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x[r]), one_hi, s1, false);
+  }
+  const bf16x2 r2 = {(bf16)s0, (bf16)s1};
+  return __builtin_bit_cast(uint32_t, r2);
 }
 
 // dS (accumulator order) -> swz8 dS^T tile [key][query]
@@ -567,59 +577,63 @@ __device__ __forceinline__ void swz_store_dst(bf16* tile, const Op<bf16>& o, int
   }
 }
 
-template <int KPW>
-__global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
-  using SM = PairSmem;
+template <int NR, int KPW>
+__global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
+  using SM = GroupSmem<NR>;
   using T = bf16;
   constexpr int KP = SM::KP;
+  constexpr int WPR = SM::WPR;        // waves per row
+  constexpr int TPR = WPR * KPW;      // key tiles of a range
+  constexpr int E = 16 / NR;          // slab values per lane in one of a tile's NR parts
+  constexpr int NQ = NR / 2;          // staging pieces per thread
+  constexpr int QBW = 4 / WPR;        // 16 x 16 dQ blocks per wave
   extern __shared__ __align__(16) char smem[];
-  T* sK = reinterpret_cast<T*>(smem);                                                     // [2][4*KPW][32][KP]
-  T* sQ = reinterpret_cast<T*>(smem + SM::k_bytes(KPW));                                  // [2][2][2][32][KP]
-  float* sLD = reinterpret_cast<float*>(smem + SM::k_bytes(KPW) + SM::qd_bytes);          // [2][2][2][32]
+  T* sK = reinterpret_cast<T*>(smem);                                                     // [NR][TPR][32][KP]
+  T* sQ = reinterpret_cast<T*>(smem + SM::k_bytes(KPW));                                  // [2][NR][2][32][KP]
+  float* sLD = reinterpret_cast<float*>(smem + SM::k_bytes(KPW) + SM::qd_bytes);          // [2][NR][2][32]
   T* sDT = reinterpret_cast<T*>(smem + SM::k_bytes(KPW) + SM::qd_bytes + SM::ld_bytes);   // [2][8][KPW][32][KP]
 
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: tile addresses stay scalar
-  const int rg = w >> 2, ww = w & 3;                       // row of the pair, wave within the row
-  const int npairs = (G.n_rows + 1) / 2;
-  const int item = xcd_item(blockIdx.x, a.nsplit * npairs * G.H);
-  const int split = item % a.nsplit, pr = (item / a.nsplit) % npairs, h = item / (a.nsplit * npairs);
-  const int tps = (nt + a.nsplit - 1) / a.nsplit;
+  const int rg = w / WPR, ww = w % WPR;                    // row of the group, wave within the row
+  const int sg = w >> 2;                                   // phase order: the two waves of a SIMD differ
+  const int ngroups = (G.n_rows + NR - 1) / NR;
+  const int item = xcd_item(blockIdx.x, a.nsplit * ngroups * G.H);
+  const int split = item % a.nsplit, gr = (item / a.nsplit) % ngroups, h = item / (a.nsplit * ngroups);
+  const int tps = (nt + a.nsplit - 1) / a.nsplit;          // at most TPR
   const int kt0 = split * tps;
   const int nkt = min(tps, nt - kt0);
   const long long headq = (long long)h * n * C;
-  const int row = 2 * pr + rg;
+  const int row = NR * gr + rg;
   const bool rvalid = row < G.n_rows;
   const int rowc = rvalid ? row : G.n_rows - 1;            // clamped: loads stay in range
   const long long irow = ((long long)rowc * G.H + h) * n;
-  const T* qrow = a.q + rowc * G.qkv_row + headq;
   const bool degen = !row_has_valid_key(a.mask, G, rowc, lane);
   const bool active = rvalid && !degen;
 
-  // K of both rows' key ranges into LDS
-  constexpr int KCH = 2 * 4 * KPW * TILE * 4;              // 16-byte pieces
+  // K of the group's rows' key ranges into LDS
+  constexpr int KCH = NR * TPR * TILE * 4;                 // 16-byte pieces
   for (int idx = tid; idx < KCH; idx += 512) {
-    const int rr = idx / (4 * KPW * TILE * 4), rem = idx % (4 * KPW * TILE * 4);
+    const int rr = idx / (TPR * TILE * 4), rem = idx % (TPR * TILE * 4);
     const int kl = rem / 4, ch = rem % 4, key = kt0 * TILE + kl;
-    const int rrow = min(2 * pr + rr, G.n_rows - 1);
+    const int rrow = min(NR * gr + rr, G.n_rows - 1);
     V16 val = {0u, 0u, 0u, 0u};
     if (kl < nkt * TILE && key < n)
       val = *reinterpret_cast<const V16*>(a.k + rrow * G.qkv_row + headq + key * G.qkv_pos + ch * 8);
-    *reinterpret_cast<V16*>(sK + (rr * 4 * KPW + kl / TILE) * TILE * KP + swz16(kl % TILE, ch * 8)) = val;
+    *reinterpret_cast<V16*>(sK + (rr * TPR + kl / TILE) * TILE * KP + swz16(kl % TILE, ch * 8)) = val;
   }
-  const T* sKr = sK + rg * 4 * KPW * TILE * KP;           // this row's K tiles
+  const T* sKr = sK + rg * TPR * TILE * KP;               // this row's K tiles
   Op<T> vb[KPW];
   uint32_t kbits[KPW];
   f32x16 dkt[KPW], dvt[KPW];
 #pragma unroll
   for (int t = 0; t < KPW; t++) {
-    const int ktg = kt0 + t * 4 + ww;
-    const int kk = ktg * TILE + l32;
-    vb[t] = (t * 4 + ww < nkt && kk < n) ? load_c_op(a.v + rowc * G.qkv_row + headq + kk * G.qkv_pos, g)
-                                         : zero_op<T>();
-    kbits[t] = (active && t * 4 + ww < nkt) ? key_bits(a.mask, G, rowc, ktg * TILE, lane) : 0u;
+    const int ktl = t * WPR + ww;
+    const int kk = (kt0 + ktl) * TILE + l32;
+    vb[t] = (ktl < nkt && kk < n) ? load_c_op(a.v + rowc * G.qkv_row + headq + kk * G.qkv_pos, g) : zero_op<T>();
+    kbits[t] = (active && ktl < nkt) ? key_bits(a.mask, G, rowc, (kt0 + ktl) * TILE, lane) : 0u;
     dkt[t] = zero16();
     dvt[t] = zero16();
   }
@@ -629,25 +643,38 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   for (int t = 0; t < KPW; t++) kfull = kfull && kbits[t] == 0xffffffffu;
   kfull = __builtin_amdgcn_readfirstlane(kfull ? 1 : 0) != 0;
 
-  // staging: per thread, one 16-byte piece of a Q (q_which 0) or dA (1) tile
-  // row of one of the two rows, and that query's lse (q_which 0) or D (1)
-  const int q_row = w >> 2, q_which = (w >> 1) & 1, q_jr = (tid >> 2) & 31, q_ch = tid & 3;
-  const int q_rowc = min(2 * pr + q_row, G.n_rows - 1);
-  const T* q_base = q_which ? a.dA + ((long long)q_rowc * G.H + h) * n * C : a.q + q_rowc * G.qkv_row + headq;
+  // staging: per thread, NQ 16-byte pieces of Q (q_which 0) or dA (1) tile
+  // rows (piece u: row (tid >> 8) + 2u of the group), and each piece's
+  // query's lse (q_which 0) or D (1)
+  const int q_which = (w >> 1) & 1, q_jr = (tid >> 2) & 31, q_ch = tid & 3;
+  const T* q_base[NQ];
+  const float* l_src[NQ];
+#pragma unroll
+  for (int u = 0; u < NQ; u++) {
+    const int q_rowc = min(NR * gr + (w >> 2) + 2 * u, G.n_rows - 1);
+    q_base[u] = q_which ? a.dA + ((long long)q_rowc * G.H + h) * n * C : a.q + q_rowc * G.qkv_row + headq;
+    l_src[u] = (q_which ? a.Dsum : a.lse) + ((long long)q_rowc * G.H + h) * n;
+  }
   const long long q_pos = q_which ? C : G.qkv_pos;
-  const float* l_src = (q_which ? a.Dsum : a.lse) + ((long long)q_rowc * G.H + h) * n;
-  V16 qpre;
-  float lpre;
+  V16 qpre[NQ];
+  float lpre[NQ];
   auto issue_q = [&](int jt) __attribute__((always_inline)) {
     const int jj = min(jt * TILE + q_jr, n - 1);
-    qpre = reinterpret_cast<const V16*>(q_base + jj * q_pos)[q_ch];
-    lpre = l_src[jj];
+#pragma unroll
+    for (int u = 0; u < NQ; u++) {
+      qpre[u] = reinterpret_cast<const V16*>(q_base[u] + jj * q_pos)[q_ch];
+      lpre[u] = l_src[u][jj];
+    }
   };
   auto stash_q = [&](int buf, int jt) __attribute__((always_inline)) {
-    *reinterpret_cast<V16*>(sQ + ((buf * 2 + q_row) * 2 + q_which) * TILE * KP + swz16(q_jr, q_ch * 8)) = qpre;
-    if (q_ch == 0)
-      sLD[((buf * 2 + q_row) * 2 + q_which) * TILE + q_jr] =
-          q_which == 0 ? (jt * TILE + q_jr < n ? lpre * LOG2E : POS_INF) : -lpre;
+#pragma unroll
+    for (int u = 0; u < NQ; u++) {
+      const int qr = (w >> 2) + 2 * u;
+      *reinterpret_cast<V16*>(sQ + ((buf * NR + qr) * 2 + q_which) * TILE * KP + swz16(q_jr, q_ch * 8)) = qpre[u];
+      if (q_ch == 0)
+        sLD[((buf * NR + qr) * 2 + q_which) * TILE + q_jr] =
+            q_which == 0 ? (jt * TILE + q_jr < n ? lpre[u] * LOG2E : POS_INF) : -lpre[u];
+    }
   };
 
   // tile addresses: a workgroup-uniform tile base plus this lane's 16 values
@@ -657,15 +684,18 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     const long long tile = (jt < nt && ktl < nkt) ? ((long long)h * nt + jt) * nt + kt0 + ktl : (long long)G.H * nt * nt;
     return reinterpret_cast<const _Float16*>(a.bias_prep) + tile * 1024 + lane16;
   };
-  T* slab_pair = a.tslab + ((long long)pr * G.H + h) * nt * nt * 1024;
-  // this wave's dQ block (transposed MFMA output): query 16 qb + (lane & 15),
-  // channels dq_c .. dq_c + 3.  The partials are padded (rows to even, queries
-  // to whole tiles), so every lane stores there, the wave's block as 512
-  // contiguous bytes; the final dQ (one key range) sends the lanes past the
-  // row's end to the trash area.
-  const int qb = ww >> 1, cb = ww & 1;
-  const int dq_c = 16 * cb + 4 * (lane >> 4);
-  T* dq_part_blk = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 16 * qb, 16 * cb) + (lane & 15) * 16 + 4 * (lane >> 4);
+  T* slab_grp = a.tslab + ((long long)gr * G.H + h) * nt * nt * 1024;
+  // this wave's dQ blocks (transposed MFMA output): query 16 qb + (lane & 15),
+  // channels 16 cb(i) + 4 (lane >> 4) + 0..3.  The partials are padded (rows
+  // to a multiple of four, queries to whole tiles), so every lane stores
+  // there, each block as 512 contiguous bytes; the final dQ (one key range)
+  // sends the lanes past the row's end to the trash area.
+  const int qb = (ww * QBW) >> 1;
+  T* dq_part_blk[QBW];
+#pragma unroll
+  for (int i = 0; i < QBW; i++)
+    dq_part_blk[i] = reinterpret_cast<T*>(a.dq_part) + dq_part_off(G, split, row, h, 16 * qb, 16 * ((ww * QBW + i) & 1)) +
+                     (lane & 15) * 16 + 4 * (lane >> 4);
   T* dq_trash = reinterpret_cast<T*>(a.trash + 1024) + 4 * tid;
 
   // bias tiles: one register set per key tile of the wave, reloaded with the
@@ -676,10 +706,10 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   // the dS^T tile (buffer jt & 1)
   auto phase1 = [&](int jt) __attribute__((always_inline)) {
     const int b = jt & 1;
-    const T* tq = sQ + ((b * 2 + rg) * 2 + 0) * TILE * KP;
-    const T* tda = sQ + ((b * 2 + rg) * 2 + 1) * TILE * KP;
-    const float* tl = sLD + ((b * 2 + rg) * 2 + 0) * TILE + 4 * g;
-    const float* td = sLD + ((b * 2 + rg) * 2 + 1) * TILE + 4 * g;
+    const T* tq = sQ + ((b * NR + rg) * 2 + 0) * TILE * KP;
+    const T* tda = sQ + ((b * NR + rg) * 2 + 1) * TILE * KP;
+    const float* tl = sLD + ((b * NR + rg) * 2 + 0) * TILE + 4 * g;
+    const float* td = sLD + ((b * NR + rg) * 2 + 1) * TILE + 4 * g;
     const Op<T> qa = swz_c_op(tq, l32, g);
     const Op<T> daa = swz_c_op(tda, l32, g);
     const Op<T> qt = swz_tr_op_m(tq, lane);
@@ -703,7 +733,7 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     for (int t = 0; t < KPW; t++) {
       f32x16 s_next, dp_next;
       if (t + 1 < KPW) {
-        const int kn = (t + 1) * 4 + ww;
+        const int kn = (t + 1) * WPR + ww;
         s_next = mma32(qa, swz_c_op(sKr + kn * TILE * KP, l32, g), bpf[t + 1]);
         bpf[t + 1] = load_tile16_h(bias_ptr(jt + 1, kn));
       }
@@ -736,53 +766,72 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
     }
   };
   // phase 2 of query tile jt (its dS^T tiles complete in buffer jt & 1):
-  // (a) this wave's 16 x 16 dQ block over all key tiles of its row
-  // (16x16x32 MFMAs); (b) the pair-bias slab = dS of row i + dS of row i+1
-  // (rounded operands, added in row order), this wave storing half rg of each
+  // (a) this wave's 16 x 16 dQ blocks over all key tiles of its row
+  // (16x16x32 MFMAs); (b) the pair-bias slab = sum of the group's NR dS tiles
+  // (rounded operands, added in row order), this wave storing part rg of each
   // of its tiles
   auto phase2 = [&](int jt) __attribute__((always_inline)) {
     const int b = jt & 1;
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 acc[QBW];
 #pragma unroll
-    for (int k8 = 0; k8 < 4 * KPW; k8++) {
-      const T* dtile = sDT + ((b * 8 + rg * 4 + (k8 & 3)) * KPW + (k8 >> 2)) * TILE * KP;
+    for (int i = 0; i < QBW; i++) acc[i] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kl = 0; kl < TPR; kl++) {
+      const T* dtile = sDT + ((b * 8 + rg * WPR + kl % WPR) * KPW + kl / WPR) * TILE * KP;
       const bf16x8 aop = swz_tr_op16<true>(dtile, 16 * qb, lane);
-      const bf16x8 bop = swz_tr_op16<false>(sKr + k8 * TILE * KP, 16 * cb, lane);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop, aop, acc, 0, 0, 0);  // (dS K)^T block
+#pragma unroll
+      for (int i = 0; i < QBW; i++) {
+        const bf16x8 bop = swz_tr_op16<false>(sKr + kl * TILE * KP, 16 * ((ww * QBW + i) & 1), lane);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bop, aop, acc[i], 0, 0, 0);  // (dS K)^T block
+      }
     }
-    // acc[i]: channel dq_c + i of query jj
+    // acc[i][e]: channel 16 cb(i) + 4 (lane >> 4) + e of query jj
     const int jj = jt * TILE + 16 * qb + (lane & 15);
-    if (a.nsplit > 1) {
-      // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
-      *reinterpret_cast<bf16x4*>(dq_part_blk + jt * 2 * 512) =
-          (bf16x4){(bf16)acc[0], (bf16)acc[1], (bf16)acc[2], (bf16)acc[3]};
-    } else {
-      T* dst = rvalid && jj < n ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : dq_trash;
-      *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(acc[0] * INV_SQRT_C), (bf16)(acc[1] * INV_SQRT_C),
-                                                 (bf16)(acc[2] * INV_SQRT_C), (bf16)(acc[3] * INV_SQRT_C)};
+#pragma unroll
+    for (int i = 0; i < QBW; i++) {
+      if (a.nsplit > 1) {
+        // partial of this key range, rounded once to bf16 (summed in fp32 by dq_sum_kernel)
+        *reinterpret_cast<bf16x4*>(dq_part_blk[i] + jt * 2 * 512) =
+            (bf16x4){(bf16)acc[i][0], (bf16)acc[i][1], (bf16)acc[i][2], (bf16)acc[i][3]};
+      } else {
+        const int dq_c = 16 * ((ww * QBW + i) & 1) + 4 * (lane >> 4);
+        T* dst = rvalid && jj < n ? a.dq + rowc * G.qkv_row + headq + jj * G.qkv_pos + dq_c : dq_trash;
+        *reinterpret_cast<bf16x4*>(dst) = (bf16x4){(bf16)(acc[i][0] * INV_SQRT_C), (bf16)(acc[i][1] * INV_SQRT_C),
+                                                   (bf16)(acc[i][2] * INV_SQRT_C), (bf16)(acc[i][3] * INV_SQRT_C)};
+      }
     }
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
-      const int ktl = t * 4 + ww;
-      const T* d0 = sDT + ((b * 8 + ww) * KPW + t) * TILE * KP;
-      const T* d1 = sDT + ((b * 8 + 4 + ww) * KPW + t) * TILE * KP;
-      const int c0 = 16 * rg + 4 * g;
-      const V8 x0 = *reinterpret_cast<const V8*>(d0 + swz8(l32, c0));
-      const V8 x1 = *reinterpret_cast<const V8*>(d0 + swz8(l32, c0 + 8));
-      const V8 y0 = *reinterpret_cast<const V8*>(d1 + swz8(l32, c0));
-      const V8 y1 = *reinterpret_cast<const V8*>(d1 + swz8(l32, c0 + 8));
-      const V16 sum = {add_bf16x2(x0[0], y0[0]), add_bf16x2(x0[1], y0[1]), add_bf16x2(x1[0], y1[0]),
-                       add_bf16x2(x1[1], y1[1])};
-      T* dst = (ktl < nkt ? slab_pair + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) +
-               rg * SLAB_HALF + lane * 8;  // this wave's half of the tile: whole lines
-      *reinterpret_cast<V16*>(dst) = sum;
+      const int ktl = t * WPR + ww;
+      // part rg of key tile ktl: accumulator registers rg*E .. rg*E+E-1, i.e.
+      // queries 4g + 8(rg*E/4 + m) + 0..3 of every row's dS^T tile (m < E/4)
+      uint32_t sum[E / 2];
+#pragma unroll
+      for (int m = 0; m < E / 4; m++) {
+        uint32_t x0[NR], x1[NR];
+#pragma unroll
+        for (int r = 0; r < NR; r++) {
+          const T* dr = sDT + ((b * 8 + r * WPR + ww) * KPW + t) * TILE * KP;
+          const V8 v = *reinterpret_cast<const V8*>(dr + swz8(l32, 4 * g + 8 * (rg * (E / 4) + m)));
+          x0[r] = v[0];
+          x1[r] = v[1];
+        }
+        sum[2 * m] = sum_rows_bf16x2<NR>(x0);
+        sum[2 * m + 1] = sum_rows_bf16x2<NR>(x1);
+      }
+      T* dst = (ktl < nkt ? slab_grp + (long long)(jt * nt + kt0 + ktl) * 1024 : reinterpret_cast<T*>(a.trash)) +
+               rg * 64 * E + lane * E;  // this wave's part of the tile: whole lines
+      if constexpr (E == 8)
+        *reinterpret_cast<V16*>(dst) = (V16){sum[0], sum[1], sum[2], sum[3]};
+      else
+        *reinterpret_cast<V8*>(dst) = (V8){sum[0], sum[1]};
     }
   };
 
   issue_q(0);
   stash_q(0, 0);
 #pragma unroll
-  for (int t = 0; t < KPW; t++) bpf[t] = load_tile16_h(bias_ptr(0, t * 4 + ww));
+  for (int t = 0; t < KPW; t++) bpf[t] = load_tile16_h(bias_ptr(0, t * WPR + ww));
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
   issue_q(1);
@@ -791,32 +840,33 @@ __global__ __launch_bounds__(512, 1) void bwd_pair_kernel(BwdArgs<bf16> a) {
   issue_q(2);
   __syncthreads();
   // Between two barriers each wave runs phase 1 of tile jt and phase 2 of tile
-  // jt - 1 (whose dS^T tiles sit in the other buffer): row group 0 in that
-  // order, row group 1 in the opposite order, so the two waves that share a
-  // SIMD (one of each group) run different instruction mixes at the same time
-  // instead of competing for the same units.  Both groups run one loop text,
-  // phase 1 (tile jt) then phase 2: group 0 takes phase 2 of tile jt - 1 before
-  // its barrier, group 1 takes its barrier first and then phase 2 of tile jt.
-  // One text keeps every accumulator in the same registers on both groups.
-  if (rg == 1) phase2(0);
+  // jt - 1 (whose dS^T tiles sit in the other buffer): waves 0-3 in that
+  // order, waves 4-7 in the opposite order, so the two waves that share a SIMD
+  // (w and w + 4) run different instruction mixes at the same time instead of
+  // competing for the same units.  Both run one loop text, phase 1 (tile jt)
+  // then phase 2: waves 0-3 take phase 2 of tile jt - 1 before their barrier,
+  // waves 4-7 take their barrier first and then phase 2 of tile jt.  One text
+  // keeps every accumulator in the same registers on both.
+  if (sg == 1) phase2(0);
   // The staging registers are stored to LDS right after phase 1 and reloaded
   // with the tile after next at once: each load has a whole iteration to land.
   for (int jt = 1; jt < nt; jt++) {
     phase1(jt);
     stash_q((jt + 1) & 1, jt + 1);
     issue_q(jt + 2);  // clamped rows: past the last tile it reloads the last one, never used
-    if (rg == 1) __syncthreads();
-    phase2(jt - 1 + rg);
-    if (rg == 0) __syncthreads();
+    if (sg == 1) __syncthreads();
+    phase2(jt - 1 + sg);
+    if (sg == 0) __syncthreads();
   }
-  if (rg == 0) phase2(nt - 1);
+  if (sg == 0) phase2(nt - 1);
 
   // dK and dV of this wave's key tiles (a fully masked row: dV = mean of dA, dK = 0)
   if (!rvalid) return;
 #pragma unroll
   for (int t = 0; t < KPW; t++) {
-    const int kk = (kt0 + t * 4 + ww) * TILE + l32;
-    if (t * 4 + ww >= nkt || kk >= n) continue;
+    const int ktl = t * WPR + ww;
+    const int kk = (kt0 + ktl) * TILE + l32;
+    if (ktl >= nkt || kk >= n) continue;
     const long long off = rowc * G.qkv_row + headq + kk * G.qkv_pos;
     if (degen) {
       for (int c = 16 * g; c < 16 * g + 16; c++) {
@@ -893,8 +943,10 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per slab
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= per_row / 8) return;
-  const long long e0 = t * 8;  // first element: [h][jt][kt][half][lane][8], r0 = 8 * half
-  const int r0 = (int)((e0 >> 9) & 1) * 8, lane = (int)((e0 >> 3) & 63);
+  // first element: [h][jt][kt][part][lane][E] with E = a.slab_e values per
+  // lane and part (E = 8: one lane's half; E = 4: two lanes' quarters)
+  const long long e0 = t * 8;
+  const int within = (int)(e0 & 1023);
   const long long tile = e0 >> 10;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
   float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -915,12 +967,12 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) s[i] += v[i];
   }
-  const int k = kt * TILE + (lane & 31), g = lane >> 5;
-  if (k >= n) return;
+  const int E = a.slab_e;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
-    const int j = jt * TILE + mrow(g, r0 + i);
-    if (j < n) a.dbias[(long long)h * n * n + j * G.bias_q + k * G.bias_k] = from_f<T>(s[i]);
+    const int off = within + i, part = off / (64 * E), ln = (off / E) & 63, r = part * E + off % E;
+    const int k = kt * TILE + (ln & 31), j = jt * TILE + mrow(ln >> 5, r);
+    if (j < n && k < n) a.dbias[(long long)h * n * n + j * G.bias_q + k * G.bias_k] = from_f<T>(s[i]);
   }
 }
 
@@ -966,10 +1018,10 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
 }
 
 
-size_t pair_smem(int kpw) { return PairSmem::total(kpw); }
+size_t group_smem(int kpw) { return GroupSmem<BF16_GROUP_ROWS>::total(kpw); }
 
 template <int KPW>
-hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* ev) {
+hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* ev) {
   const Geo& G = a.geo;
   const int nt = (G.n + TILE - 1) / TILE;
   hipError_t e;
@@ -985,13 +1037,14 @@ hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* e
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;
   if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)bwd_pair_kernel<KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)PairSmem::total(KPW));
+    e = hipFuncSetAttribute((const void*)bwd_group_kernel<BF16_GROUP_ROWS, KPW>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GroupSmem<BF16_GROUP_ROWS>::total(KPW));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int npairs = (G.n_rows + 1) / 2;
-  hipLaunchKernelGGL((bwd_pair_kernel<KPW>), dim3(a.nsplit * npairs * G.H), dim3(512), PairSmem::total(KPW), st, a);
+  const int ngroups = (G.n_rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS;
+  hipLaunchKernelGGL((bwd_group_kernel<BF16_GROUP_ROWS, KPW>), dim3(a.nsplit * ngroups * G.H), dim3(512),
+                     GroupSmem<BF16_GROUP_ROWS>::total(KPW), st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_threads = (long long)G.H * nt * nt * 128;
@@ -1007,8 +1060,8 @@ hipError_t launch_bwd_pair(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* e
   return hipSuccess;
 }
 
-template hipError_t launch_bwd_pair<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_pair<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_group<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_group<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 
 template hipError_t launch_bwd_tile<bf16, 1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<bf16, 2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);

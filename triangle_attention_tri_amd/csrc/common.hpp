@@ -271,14 +271,16 @@ template <typename T> struct FwdArgs {
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;
+constexpr int BF16_GROUP_ROWS = 4;  // rows per workgroup of the bf16 backward (2 or 4)
 
 // dQ partials of the key ranges: per (range, row, h) a block of whole 32-query
 // tiles, each [channel half][32 queries][16 channels], so that a wave's 16 x 16
 // block of a tile (16 queries, one channel half) is 512 contiguous bytes.  The
-// row count is rounded up to even and the query count up to whole tiles, so a
-// two-row workgroup stores every lane of a tile without a bounds select (the
+// row count is rounded up to a multiple of four and the query count up to
+// whole tiles, so a row-group workgroup stores every lane of a tile without a
+// bounds select (the
 // padding is written, never read).
-__host__ __device__ inline long long dq_part_rows(int n_rows) { return n_rows + (n_rows & 1); }
+__host__ __device__ inline long long dq_part_rows(int n_rows) { return (n_rows + 3) & ~3; }
 __host__ __device__ inline long long dq_part_queries(int n) { return (long long)((n + TILE - 1) / TILE) * TILE; }
 __device__ __forceinline__ long long dq_part_off(const Geo& G, int split, int row, int h, int jj, int c) {
   return ((split * dq_part_rows(G.n_rows) + row) * G.H + h) * dq_part_queries(G.n) * C +
@@ -302,7 +304,8 @@ template <typename T> struct BwdArgs {
   float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
                      // the tile loop's memory instructions do not depend on branches
   int nsplit;        // key-range splits per row in the tile kernel
-  int slab_rows;     // row slabs of dS tiles the dbias reduction sums (rows, or row pairs)
+  int slab_rows;     // row slabs of dS tiles the dbias reduction sums (rows, or row groups)
+  int slab_e;        // slab tile layout [16 / slab_e parts][64 lanes][slab_e values]
 };
 
 // 16 consecutive floats (64 bytes, 16-byte aligned) as one accumulator tile's
