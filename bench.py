@@ -285,7 +285,7 @@ def main():
     dom = max(("fwd", "bwd_main"), key=lambda k: stages[k])
     bound, work = algo[dom]
     achieved = work / (stages[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_pair_kernel"}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_group_kernel"}
     roofline = {"kernel": kernel_names[dom], "bound": bound, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": stored_traffic(kernel_names[dom]), "launch_ms": round(stages[dom], 4)}
