@@ -271,8 +271,9 @@ def test_determinism_n768(device):
 # --------------------------------------------------------------------------- other paths
 @pytest.mark.parametrize("n,dtype", [(300, torch.float32), (960, torch.bfloat16), (736, torch.float32)])
 def test_row_group_backward_sizes(device, n, dtype):
-    """Sizes past the per-row tile kernel's limit (fp32 n > 256, bf16 n > 768) take the
-    row-group backward; the largest accepted n of each dtype is included."""
+    """Largest sizes of each backward path: fp32 past the per-row tile kernel's limit
+    (n > 256) takes the fallback rows kernel; bf16 n = 960 (the largest accepted) runs the
+    group kernel with eight key ranges."""
     assert n <= ta.max_n(dtype)
     log(f"row-group backward n={n} dtype={dtype}")
     xc = inputs.attn_inputs(n, 4, 32, dtype, seed=200 + n, bias_std=1.5)
