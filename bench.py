@@ -28,12 +28,21 @@ PEAK_HBM_GBS = 8000.0
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-class Hip:
-    """Minimal HIP event API through ctypes (events on the stream torch uses)."""
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
-    def __init__(self):
+
+class Hip:
+    """Minimal HIP event API through ctypes (events on the stream torch uses).
+
+    The events only time work on the GPU, so they are created without the
+    system-scope fence: recording one then costs no cache write-back and
+    invalidation between the kernels it separates.
+    """
+
+    def __init__(self, event_flags: int = HIP_EVENT_DISABLE_SYSTEM_FENCE):
         self.lib = ctypes.CDLL("libamdhip64.so")
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.flags = event_flags
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
@@ -41,7 +50,7 @@ class Hip:
 
     def event(self):
         e = ctypes.c_void_p()
-        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.flags) == 0
         return e
 
     def record(self, e, stream):
