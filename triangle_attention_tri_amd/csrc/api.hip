@@ -63,6 +63,8 @@ int check_common(int n_rows, int n, int h, int c, int dtype, int ending) {
   if (ending != 0 && ending != 1) return TRI_ATTN_EINVAL;
   if (c != C) return TRI_ATTN_EUNSUPPORTED;
   if ((long long)n * n * h > (1ll << 40)) return TRI_ATTN_EUNSUPPORTED;
+  // the forward stages K / V at a 32-bit byte stride per key position (h*n*c elements at the ending node)
+  if ((long long)h * n * C * 4 >= (1ll << 32)) return TRI_ATTN_EUNSUPPORTED;
   if (n > max_n(dtype)) return TRI_ATTN_EUNSUPPORTED;
   return TRI_ATTN_OK;
 }

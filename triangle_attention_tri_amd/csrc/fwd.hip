@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias
     const int k = kt * TILE + mrow(g, r);
     v[r] = (j < G.n && k < G.n) ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C : 0.0f;
   }
-  if constexpr (sizeof(T) == 4) {
+  if constexpr (sizeof(bias_store_t<T>) == 4) {
     f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
 #pragma unroll
     for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
@@ -105,12 +105,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
   const bias_store_t<T>* biasp = reinterpret_cast<const bias_store_t<T>*>(a.bias_prep) +
                                  ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 16;
 
-  // key masks: one word per (row, key tile); keys past n are never kept
-  for (int idx = w; idx < R * nt; idx += 4) {
-    const int rr = idx / nt, kt = idx % nt;
-    const int row = min(row0 + rr, G.n_rows - 1);
-    const uint32_t bits = key_bits(a.mask, G, row, kt * TILE, lane);
-    if (lane == 0) sMask[rr][kt] = bits;
+  // key masks: one word per (row, key tile); keys past n are never kept.
+  // Without a mask only the key count decides, one word per thread.
+  if (a.mask == nullptr) {
+    for (int idx = tid; idx < R * nt; idx += 256) {
+      const int left = n - (idx % nt) * TILE;
+      sMask[idx / nt][idx % nt] = left >= TILE ? 0xffffffffu : ((1u << left) - 1u);
+    }
+  } else {
+    for (int idx = w; idx < R * nt; idx += 4) {
+      const int rr = idx / nt, kt = idx % nt;
+      const int row = min(row0 + rr, G.n_rows - 1);
+      const uint32_t bits = key_bits(a.mask, G, row, kt * TILE, lane);
+      if (lane == 0) sMask[rr][kt] = bits;
+    }
   }
 
   Op<T> qop[R];
@@ -129,17 +137,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
   }
 
   // K / V staging: every load is unconditional (row and key clamped into range;
-  // keys past n are masked out, rows past n_rows are never computed)
+  // keys past n are masked out, rows past n_rows are never computed).  A
+  // thread's pieces have a fixed (K or V, row, key, chunk), so the address is a
+  // per-thread base plus key * (bytes per key position), one 32 x 32 -> 64-bit
+  // multiply-add; the host keeps that stride below 2^32 bytes.
   V16 pre[LPT];
+  const char* src[LPT];
+  int skey[LPT];
+  const uint32_t pos_bytes = (uint32_t)(G.qkv_pos * (long long)sizeof(T));
+#pragma unroll
+  for (int q = 0; q < LPT; q++) {
+    const int idx = tid + 256 * q;
+    const int ch = idx % CHUNKS, rr = (idx / (CHUNKS * TILE)) % R, isv = idx / (CHUNKS * TILE * R);
+    const int row = min(row0 + rr, G.n_rows - 1);
+    skey[q] = (idx / CHUNKS) % TILE;
+    src[q] = reinterpret_cast<const char*>((isv ? a.v : a.k) + row * G.qkv_row + headq + ch * EPV);
+  }
   auto issue = [&](int kt_in) __attribute__((always_inline)) {
-    const int kt = min(kt_in, nt - 1);
+    const int k0 = min(kt_in, nt - 1) * TILE;
 #pragma unroll
     for (int q = 0; q < LPT; q++) {
-      const int idx = tid + 256 * q;
-      const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, rr = (idx / (CHUNKS * TILE)) % R;
-      const int isv = idx / (CHUNKS * TILE * R);
-      const int row = min(row0 + rr, G.n_rows - 1), kk = min(kt * TILE + key, n - 1);
-      pre[q] = *reinterpret_cast<const V16*>((isv ? a.v : a.k) + row * G.qkv_row + headq + kk * G.qkv_pos + ch * EPV);
+      const uint32_t kk = (uint32_t)min(k0 + skey[q], n - 1);
+      pre[q] = *reinterpret_cast<const V16*>(src[q] + (uint64_t)kk * pos_bytes);
     }
   };
   auto stash = [&](int buf) __attribute__((always_inline)) {
