@@ -109,15 +109,11 @@ __global__ __launch_bounds__(256) void bwd_pre_vec_kernel(BwdArgs<T> a) {
   if (live && part == 0) a.Dsum[((long long)row * G.H + h) * G.n + j] = dsum;
 }
 
-// bias prep for the backward tile orientation (lane = key):
-// out[h][jt][kt][lane][r] = sqrt(c) * bias(j = jt*32 + mrow(lane>>5, r), k = kt*32 + (lane & 31)),
-// stored as B: fp32 for fp32 runs; fp16 for bf16 runs, whose main kernel then
-// moves half the bytes per tile.  fp16 keeps 11 significant bits, so the scaled
-// bias is off by at most 2^-12 of itself (2^-12 |b| in logit units, four times
-// finer than the bf16 input's own spacing); it saturates at +-65504, i.e. for
-// |b| beyond 65504 / sqrt(c) ~ 11580.
-template <typename T, typename B>
-__global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias, B* out) {
+// fp32 bias prep for the backward tile orientation (lane = key):
+// out[h][jt][kt][lane][r] = sqrt(c) * bias(j = jt*32 + mrow(lane>>5, r), k = kt*32 + (lane & 31)).
+// (bf16 runs add the bias with MFMAs from the operand tiles of launch_bias_op_prep.)
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias, float* out) {
   const int nt = (G.n + TILE - 1) / TILE;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long total = (long long)G.H * nt * nt * 64;
@@ -138,20 +134,9 @@ __global__ __launch_bounds__(256) void bwd_bias_prep_kernel(Geo G, const T* bias
                                   : 0.0f;
     }
   }
-  if constexpr (sizeof(B) == 4) {
-    f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
 #pragma unroll
-    for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-  } else {
-    f16x8* o = reinterpret_cast<f16x8*>(out + t * 16);
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-      f16x8 x;
-#pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = (_Float16)fminf(fmaxf(v[8 * q + e], -65504.0f), 65504.0f);
-      o[q] = x;
-    }
-  }
+  for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
 // dS slab tiles (1024 values, accumulator order) are laid out [half][lane][8]:
@@ -682,7 +667,7 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
   auto bias_ptr = [&](int jt, int ktl) __attribute__((always_inline)) {
     // past the key range or the last query tile: the zero tile after the heads' tiles
     const long long tile = (jt < nt && ktl < nkt) ? ((long long)h * nt + jt) * nt + kt0 + ktl : (long long)G.H * nt * nt;
-    return reinterpret_cast<const _Float16*>(a.bias_prep) + tile * 1024 + lane16;
+    return reinterpret_cast<const bf16*>(a.bias_prep) + tile * 1024 + lane16;
   };
   T* slab_grp = a.tslab + ((long long)gr * G.H + h) * nt * nt * 1024;
   // this wave's dQ blocks (transposed MFMA output): query 16 qb + (lane & 15),
@@ -698,10 +683,12 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
                      (lane & 15) * 16 + 4 * (lane >> 4);
   T* dq_trash = reinterpret_cast<T*>(a.trash + 1024) + 4 * tid;
 
-  // bias tiles: one register set per key tile of the wave, reloaded with the
-  // next query tile's tile as soon as the logit MFMA has taken it as its
-  // accumulator input, so every load has a whole iteration to land
-  f32x16 bpf[KPW];
+  // bias operand tiles: one register set per key tile of the wave, reloaded
+  // with the next query tile's tile as soon as the logit MFMAs have taken it,
+  // so every load has a whole iteration to land.  The logits start from the
+  // bias term (bias tile x sqrt(c) I, two MFMAs), then add Q K^T.
+  Op<T> bpf[KPW];
+  const Op<T> ident = sqrtc_identity(lane);
   // phase 1 of query tile jt: per key tile, S and P recomputed once; dV, dK and
   // the dS^T tile (buffer jt & 1)
   auto phase1 = [&](int jt) __attribute__((always_inline)) {
@@ -726,16 +713,16 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
     // key tile t + 1 are issued before the exponentials of tile t (and dP - D
     // of tile 0 with its logits), so the matrix pipe runs them while the
     // VALU works.  The scheduling barrier keeps that order.
-    f32x16 s_cur = mma32(qa, swz_c_op(sKr + ww * TILE * KP, l32, g), bpf[0]);
-    bpf[0] = load_tile16_h(bias_ptr(jt + 1, ww));
+    f32x16 s_cur = mma32(qa, swz_c_op(sKr + ww * TILE * KP, l32, g), mma32(bpf[0], ident, zero16()));
+    bpf[0] = load_bias_op(bias_ptr(jt + 1, ww));
     f32x16 dp_cur = mma32(daa, vb[0], dng);
 #pragma unroll
     for (int t = 0; t < KPW; t++) {
       f32x16 s_next, dp_next;
       if (t + 1 < KPW) {
         const int kn = (t + 1) * WPR + ww;
-        s_next = mma32(qa, swz_c_op(sKr + kn * TILE * KP, l32, g), bpf[t + 1]);
-        bpf[t + 1] = load_tile16_h(bias_ptr(jt + 1, kn));
+        s_next = mma32(qa, swz_c_op(sKr + kn * TILE * KP, l32, g), mma32(bpf[t + 1], ident, zero16()));
+        bpf[t + 1] = load_bias_op(bias_ptr(jt + 1, kn));
       }
       __builtin_amdgcn_sched_barrier(0);
       f32x16 p;
@@ -831,7 +818,7 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
   issue_q(0);
   stash_q(0, 0);
 #pragma unroll
-  for (int t = 0; t < KPW; t++) bpf[t] = load_tile16_h(bias_ptr(0, t * WPR + ww));
+  for (int t = 0; t < KPW; t++) bpf[t] = load_bias_op(bias_ptr(0, t * WPR + ww));
   __syncthreads();
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): only the loop's own prefetches in flight at its head
   issue_q(1);
@@ -1005,7 +992,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
-  hipLaunchKernelGGL((bwd_bias_prep_kernel<T, float>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
                      G, a.bias, a.bias_prep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
@@ -1045,10 +1032,7 @@ hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* 
   hipLaunchKernelGGL((bwd_pre_vec_kernel<bf16>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
-  hipLaunchKernelGGL((bwd_bias_prep_kernel<bf16, _Float16>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256),
-                     0, st, G, a.bias, reinterpret_cast<_Float16*>(a.bias_prep));
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st)) != hipSuccess) return e;
   if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;
   if (!attr_set) {

@@ -167,7 +167,6 @@ __device__ __forceinline__ void store_c_op(float* row, const Op<float>& o, int g
 // lives in registers)
 typedef uint32_t V16 __attribute__((ext_vector_type(4)));
 typedef uint32_t V8 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // Operands read from row-major LDS tiles (32 rows, `pitch` elements per row).
@@ -267,7 +266,7 @@ template <typename T> struct FwdArgs {
   const uint8_t* mask;
   T *out, *attn;
   float* lse;
-  float* bias_prep;  // workspace: sqrt(c)-scaled bias in per-lane tile order (fp32; fp16 for bf16 runs)
+  float* bias_prep;  // workspace: bias tiles in per-lane order (bf16 operand tiles; sqrt(c)-scaled fp32 in fp32 runs)
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;
@@ -297,8 +296,8 @@ template <typename T> struct BwdArgs {
   float* Dsum;     // workspace [n_rows][H][n], D = sum_c dA * attn
   float* slabs;    // workspace [groups][H][n][n] dbias partial per row group (row-group kernel)
   int groups;
-  float* bias_prep;  // workspace [H][nt][nt][64][16] sqrt(c)-scaled bias in per-lane tile order, + one zero tile
-                     // (fp32; the bf16 two-row kernel reads it as fp16)
+  float* bias_prep;  // workspace [H][nt][nt][64][16] bias tiles in per-lane order, + one zero tile
+                     // (fp32 runs: sqrt(c)-scaled fp32 accumulator tiles; bf16 runs: bf16 operand tiles)
   T* tslab;          // workspace [n_rows][H][nt][nt][64][16] dS tiles per row (tile kernel)
   void* dq_part;     // workspace [nsplit][rows, even][H][n, whole tiles][C] dQ partial per key split (nsplit > 1), in T
   float* trash;      // workspace, BWD_TRASH_BYTES: target of stores that have nothing to write, so
@@ -322,20 +321,44 @@ __device__ __forceinline__ f32x16 load_tile16(const float* base) {
   return v;
 }
 
-// one lane's 16 fp16 bias values (two 16-byte loads), widened to fp32
-__device__ __forceinline__ f32x16 load_tile16_h(const _Float16* p) {
-  const f16x8 x = reinterpret_cast<const f16x8*>(p)[0], y = reinterpret_cast<const f16x8*>(p)[1];
-  f32x16 v;
+// ---------------------------------------------------------------------------
+// Pair bias in bf16 runs: an MFMA operand, added by the matrix pipe.
+//
+// The bias term sqrt(c) * b(j, k) of a 32 x 32 logit tile is the product of
+// the bias tile with sqrt(c) times the identity, so two more 32x32x16 MFMAs
+// (a contraction of length 32 over the tile's keys) put it into the logit
+// accumulator and no VALU instruction converts or adds it.  One operand is
+// the bias tile in c-map order -- lane l holds b(j, k) for query j = j0 +
+// (l & 31) and keys k = k0 + 16u + 8(l >> 5) + e -- which a prep kernel writes
+// once per call as [h][query tile][key tile][lane][16] bf16 (zero outside n,
+// plus one zero tile after the last head).  The other is the constant
+// sqrt(c) I.  sqrt(c) = 5.65685... is held as the bf16 value 5.65625, so the
+// bias term is exact up to a relative 1.1e-4 (the bias itself is bf16 input,
+// multiplied exactly in the MFMA and accumulated in fp32).
+//
+// The forward tile is keys x queries: the identity is the A operand (rows =
+// keys) and the bias tile the B operand (columns = queries).  The backward
+// tile is queries x keys: the bias tile is the A operand (rows = queries) and
+// the identity the B operand (columns = keys).  Both read the same lane order.
+__device__ __forceinline__ Op<bf16> sqrtc_identity(int lane) {
+  const int g = lane >> 5, l32 = lane & 31;
+  Op<bf16> o;
 #pragma unroll
-  for (int e = 0; e < 8; e++) {
-    v[e] = (float)x[e];
-    v[8 + e] = (float)y[e];
-  }
-  return v;
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) o.f[u][e] = (16 * u + 8 * g + e == l32) ? (bf16)SQRT_C : (bf16)0.0f;
+  return o;
 }
-// the prepared-bias tile of a lane in its storage type, as fp32 registers
-__device__ __forceinline__ f32x16 load_bias_tile(const float* p) { return load_tile16<float>(p); }
-__device__ __forceinline__ f32x16 load_bias_tile(const _Float16* p) { return load_tile16_h(p); }
+// a lane's 16 bias values of one prepared tile (two 16-byte loads)
+__device__ __forceinline__ Op<bf16> load_bias_op(const bf16* tile_lane) {
+  Op<bf16> o;
+  o.f[0] = reinterpret_cast<const bf16x8*>(tile_lane)[0];
+  o.f[1] = reinterpret_cast<const bf16x8*>(tile_lane)[1];
+  return o;
+}
+// Writes the prepared bias tiles ([h][nt][nt][64][16] bf16 and one zero tile)
+// of a bf16 call into `out`, which holds (h nt^2 + 1) * 2048 bytes.
+hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStream_t st);
 
 // XCD-aware work order.  Workgroups are dispatched to the eight XCDs round
 // robin (workgroup b runs on XCD b % 8, each with its own L2).  This maps the

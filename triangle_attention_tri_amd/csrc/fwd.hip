@@ -7,10 +7,12 @@
 // the other half of a double-buffered LDS area, so there is one barrier per
 // key tile.  The logit tile is computed transposed (keys x queries): each lane
 // owns one query and 16 of the tile's keys, the other lane half owns the other
-// 16.  The pair-bias tile is fed to the logit MFMA as its accumulator input and
-// shared by the R rows (the bias does not depend on i); a prep kernel writes
-// it once per call, pre-scaled by sqrt(c) in fp32, in exactly the register
-// order a lane needs, so the main loop spends no VALU on it.
+// 16.  The pair-bias term is the logit MFMA's accumulator input, shared by the
+// R rows (the bias does not depend on i).  In bf16 runs two MFMAs form it per
+// key tile from the bf16 bias tile and sqrt(c) times the identity (the
+// operands are described with sqrtc_identity); in fp32 runs a prep kernel
+// writes sqrt(c) * b in fp32 in exactly the register order a lane needs.
+// Either way the main loop spends no VALU on the bias.
 //
 // Softmax.  Base 2 with a per-query reference r: p = exp2(raw*SC - r), where
 // raw = q.k + sqrt(c)*b and SC = log2(e)/sqrt(c).  The reference is the exact
@@ -35,15 +37,9 @@ template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 8 : 4; }
 
 constexpr float SUM_LIMIT = 4096.0f;  // a lane's tile sum above this moves the reference
 
-// bias prep for the forward: out[h][jt][kt][lane][r] = sqrt(c) * bias(j, k) with
-// j = jt*32 + (lane & 31), k = kt*32 + mrow(lane >> 5, r); zero outside n.
-// Stored as B: fp32 for fp32 runs, fp16 for bf16 runs (half the bytes the main
-// loop reads; 11 significant bits, i.e. the scaled bias within 2^-12 of itself,
-// saturating at +-65504).
-template <typename T> using bias_store_t = typename std::conditional<sizeof(T) == 2, _Float16, float>::type;
-
-template <typename T>
-__global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias, bias_store_t<T>* out) {
+// fp32 bias prep for the forward: out[h][jt][kt][lane][r] = sqrt(c) * bias(j, k)
+// with j = jt*32 + (lane & 31), k = kt*32 + mrow(lane >> 5, r); zero outside n.
+__global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const float* bias, float* out) {
   const int nt = (G.n + TILE - 1) / TILE;
   const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one thread per (h, jt, kt, lane)
   const long long total = (long long)G.H * nt * nt * 64;
@@ -56,22 +52,48 @@ __global__ __launch_bounds__(256) void fwd_bias_prep_kernel(Geo G, const T* bias
 #pragma unroll
   for (int r = 0; r < 16; r++) {
     const int k = kt * TILE + mrow(g, r);
-    v[r] = (j < G.n && k < G.n) ? to_f(bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k]) * SQRT_C : 0.0f;
+    v[r] = (j < G.n && k < G.n) ? bias[(long long)h * G.n * G.n + j * G.bias_q + k * G.bias_k] * SQRT_C : 0.0f;
   }
-  if constexpr (sizeof(bias_store_t<T>) == 4) {
-    f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
+  f32x4* o = reinterpret_cast<f32x4*>(out + t * 16);
 #pragma unroll
-    for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
-  } else {
-    f16x8* o = reinterpret_cast<f16x8*>(out + t * 16);
+  for (int q = 0; q < 4; q++) o[q] = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
+// bf16 bias operand prep (forward and backward): out[h][jt][kt][lane][8u + e] =
+// bias(j = jt*32 + (lane & 31), k = kt*32 + 16u + 8(lane >> 5) + e), zero
+// outside n; the 64 threads past the last head write the zero tile.
+__global__ __launch_bounds__(256) void bias_op_prep_kernel(Geo G, const bf16* bias, bf16* out) {
+  const int nt = (G.n + TILE - 1) / TILE;
+  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // one thread per (h, jt, kt, lane)
+  const long long total = (long long)G.H * nt * nt * 64;
+  if (t >= total + 64) return;
+  bf16x8 v[2];
 #pragma unroll
-    for (int q = 0; q < 2; q++) {
-      f16x8 x;
+  for (int u = 0; u < 2; u++) v[u] = (bf16x8)(0);
+  if (t < total) {
+    const int lane = (int)(t & 63);
+    const long long tile = t >> 6;
+    const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
+    const int j = jt * TILE + (lane & 31), g = lane >> 5;
+    const bf16* src = bias + (long long)h * G.n * G.n + (long long)min(j, G.n - 1) * G.bias_q;
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = (_Float16)fminf(fmaxf(v[8 * q + e], -65504.0f), 65504.0f);
-      o[q] = x;
-    }
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const int k = kt * TILE + 16 * u + 8 * g + e;
+        if (j < G.n && k < G.n) v[u][e] = src[(long long)k * G.bias_k];
+      }
   }
+  bf16x8* o = reinterpret_cast<bf16x8*>(out + t * 16);
+  o[0] = v[0];
+  o[1] = v[1];
+}
+
+hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStream_t st) {
+  const int nt = (G.n + TILE - 1) / TILE;
+  const long long threads = (long long)G.H * nt * nt * 64 + 64;
+  hipLaunchKernelGGL(bias_op_prep_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, G, bias, out);
+  return hipGetLastError();
 }
 
 // Longest key axis whose per-tile mask words fit the LDS table below.
@@ -101,9 +123,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
   const int j = jt * TILE + l32;
   const bool jvalid = j < n;
   const long long headq = (long long)h * n * C;
-  // bias tiles of this wave's query tile (a wave past the last query tile reads the last one, unused)
-  const bias_store_t<T>* biasp = reinterpret_cast<const bias_store_t<T>*>(a.bias_prep) +
-                                 ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 16;
+  // bias tiles of this wave's query tile (a wave past the last query tile reads the last one, unused):
+  // bf16 operand tiles in bf16 runs, sqrt(c)-scaled fp32 accumulator tiles in fp32 runs
+  const long long bias_lane = ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 16;
 
   // key masks: one word per (row, key tile); keys past n are never kept.
   // Without a mask only the key count decides, one word per thread.
@@ -169,13 +191,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
       *reinterpret_cast<V16*>(&sKV[buf][slot][key][ch * EPV]) = pre[q];
     }
   };
+  typedef typename std::conditional<sizeof(T) == 2, Op<bf16>, f32x16>::type BiasTile;
   auto load_bias = [&](int kt) __attribute__((always_inline)) {
-    return load_bias_tile(biasp + (long long)min(kt, nt - 1) * 64 * 16);
+    const long long off = bias_lane + (long long)min(kt, nt - 1) * 64 * 16;
+    if constexpr (sizeof(T) == 2)
+      return load_bias_op(reinterpret_cast<const bf16*>(a.bias_prep) + off);
+    else
+      return load_tile16<float>(a.bias_prep + off);
+  };
+  // the tile's bias term in accumulator form (keys x queries, sqrt(c) * b)
+  Op<bf16> ident;
+  if constexpr (sizeof(T) == 2) ident = sqrtc_identity(lane);
+  auto bias_acc = [&](const BiasTile& b) __attribute__((always_inline)) {
+    if constexpr (sizeof(T) == 2)
+      return mma32(ident, b, zero16());
+    else
+      return b;
   };
 
   // one key tile for all R rows
-  auto tile = [&](int kt, int buf, const f32x16& bias) __attribute__((always_inline)) {
+  auto tile = [&](int kt, int buf, const BiasTile& btile) __attribute__((always_inline)) {
     const int k0 = kt * TILE;
+    const f32x16 bias = bias_acc(btile);
 #pragma unroll
     for (int rr = 0; rr < R; rr++) {
       if (!rvalid[rr]) continue;
@@ -227,7 +264,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
 
   issue(0);
   stash(0);
-  f32x16 bA = load_bias(0), bB;
+  BiasTile bA = load_bias(0), bB;
   __syncthreads();
   // Two key tiles per iteration, so the two bias tiles alternate between fixed
   // registers; the prefetch is unconditional (a tile index past the end is
@@ -292,10 +329,15 @@ template <typename T, int R>
 hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
   const Geo& G = a.geo;
   const int nt = (G.n + TILE - 1) / TILE;
-  const long long prep_threads = (long long)G.H * nt * nt * 64;
-  hipLaunchKernelGGL((fwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G,
-                     a.bias, reinterpret_cast<bias_store_t<T>*>(a.bias_prep));
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if constexpr (sizeof(T) == 2) {
+    e = launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st);
+  } else {
+    const long long prep_threads = (long long)G.H * nt * nt * 64;
+    hipLaunchKernelGGL(fwd_bias_prep_kernel, dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st, G, a.bias,
+                       a.bias_prep);
+    e = hipGetLastError();
+  }
   if (e != hipSuccess) return e;
   const int blocks = ((G.n + 127) / 128) * ((G.n_rows + R - 1) / R) * G.H;
   hipLaunchKernelGGL((fwd_kernel<T, R>), dim3(blocks), dim3(256), 0, st, a);
