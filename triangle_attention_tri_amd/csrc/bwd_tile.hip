@@ -479,44 +479,6 @@ struct GroupSmem {
   }
 };
 
-// LDS swizzles of the 32 x 32 bf16 tiles (64-byte rows, no padding): the
-// element (row r, column c) lives at the returned element offset.  Each makes
-// every access pattern of its tiles free of bank conflicts (64 banks x 4 B):
-//  * swz16 (K, Q, dA tiles: 16-byte row reads and writes, transposing reads):
-//    the 16-byte chunk index is XORed with ((r >> 2) ^ (r >> 4)) & 3;
-//  * swz8 (dS^T tiles: 8-byte row writes / reads, transposing reads): the
-//    8-byte chunk index is XORed with a bit permutation of (r >> 2) & 7.
-// Both keep every 4-element (8-byte) group contiguous, and swz16 every
-// 8-element (16-byte) group.
-__device__ __forceinline__ int swz16(int r, int c) {
-  return r * TILE + ((((c >> 3) ^ (r >> 2) ^ (r >> 4)) & 3) << 3) + (c & 7);
-}
-__device__ __forceinline__ int swz8(int r, int c) {
-  const int a = (r >> 2) & 7;
-  const int t = (((a >> 1) & 1) << 2) | ((a & 1) << 1) | (a >> 2);
-  return r * TILE + ((((c >> 2) ^ t) & 7) << 2) + (c & 3);
-}
-
-// c-map operand of row `row` of a swz16 tile (contraction = the row's columns)
-__device__ __forceinline__ Op<bf16> swz_c_op(const bf16* tile, int row, int g) {
-  Op<bf16> o;
-  o.f[0] = *reinterpret_cast<const bf16x8*>(tile + swz16(row, 8 * g));
-  o.f[1] = *reinterpret_cast<const bf16x8*>(tile + swz16(row, 16 + 8 * g));
-  return o;
-}
-// MAP_M transposed operand of a swz16 tile (see lds_tr_op)
-__device__ __forceinline__ Op<bf16> swz_tr_op_m(const bf16* tile, int lane) {
-  const int G = lane >> 4, jp = lane & 15, g = lane >> 5;
-  const int col = 16 * (G & 1) + 4 * (jp & 3);
-  Op<bf16> o;
-#pragma unroll
-  for (int u = 0; u < 2; u++) {
-    const bf16x4 lo = lds_read_tr(tile + swz16(tr_row<MAP_M>(u, 0, g) + (jp >> 2), col));
-    const bf16x4 hi = lds_read_tr(tile + swz16(tr_row<MAP_M>(u, 1, g) + (jp >> 2), col));
-    o.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  }
-  return o;
-}
 // 16x16x32 operand (lane: row/column lane & 15, contraction 8 * (lane >> 4) + 0..7)
 // taken down the rows of a swizzled tile: column col0 + (lane & 15), rows
 // 8 * (lane >> 4) .. +7, via two transposing reads

@@ -33,7 +33,9 @@
 
 namespace tri {
 
-template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 8 : 4; }
+// LDS rows: bf16 tiles are unpadded and swz16-swizzled (conflict-free row
+// reads, transposing reads and staging writes); fp32 rows are padded by 4.
+template <typename T> constexpr int kpad() { return sizeof(T) == 2 ? 0 : 4; }
 
 constexpr float SUM_LIMIT = 4096.0f;  // a lane's tile sum above this moves the reference
 
@@ -100,7 +102,7 @@ hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStr
 constexpr int FWD_MAX_TILES = 64;
 
 template <typename T, int R>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void fwd_kernel(FwdArgs<T> a) {
   constexpr int KP = TILE + kpad<T>();            // LDS row pitch (elements)
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte vector
   constexpr int CHUNKS = C / EPV;                 // vectors per 32-element row
@@ -188,7 +190,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
     for (int q = 0; q < LPT; q++) {
       const int idx = tid + 256 * q;
       const int ch = idx % CHUNKS, key = (idx / CHUNKS) % TILE, slot = idx / (CHUNKS * TILE);
-      *reinterpret_cast<V16*>(&sKV[buf][slot][key][ch * EPV]) = pre[q];
+      T* tile = &sKV[buf][slot][0][0];
+      if constexpr (sizeof(T) == 2)
+        *reinterpret_cast<V16*>(tile + swz16(key, ch * EPV)) = pre[q];
+      else
+        *reinterpret_cast<V16*>(tile + key * KP + ch * EPV) = pre[q];
     }
   };
   typedef typename std::conditional<sizeof(T) == 2, Op<bf16>, f32x16>::type BiasTile;
@@ -217,7 +223,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
     for (int rr = 0; rr < R; rr++) {
       if (!rvalid[rr]) continue;
       const uint32_t mbits = sMask[rr][kt];
-      const Op<T> kop = lds_c_op(&sKV[buf][rr][l32][0], g);
+      Op<T> kop;
+      if constexpr (sizeof(T) == 2)
+        kop = swz_c_op(&sKV[buf][rr][0][0], l32, g);
+      else
+        kop = lds_c_op(&sKV[buf][rr][l32][0], g);
       f32x16 s = mma32(kop, qop[rr], bias);  // s[r]: key k0+mrow(g,r), query j (raw units)
       if (degen[rr]) {
 #pragma unroll
@@ -257,7 +267,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs<T> a) {
         lt = op_sum(pop);
       }
       l[rr] += lt;
-      const Op<T> vop = lds_tr_op<MAP_M>(&sKV[buf][R + rr][0][0], KP, lane);
+      Op<T> vop;
+      if constexpr (sizeof(T) == 2)
+        vop = swz_tr_op_m(&sKV[buf][R + rr][0][0], lane);
+      else
+        vop = lds_tr_op<MAP_M>(&sKV[buf][R + rr][0][0], KP, lane);
       o[rr] = mma32(vop, pop, o[rr]);  // o[r]: channel mrow(g,r), query j
     }
   };
