@@ -199,6 +199,7 @@ def main():
     ap.add_argument("--n", type=int, default=768)
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
+    ap.add_argument("--no-rc", action="store_true", help="skip the timing of the residual-compensated pair")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the LayerNorm + projection + attention + output-linear block timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -233,13 +234,24 @@ def main():
     fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    attn_res = torch.empty((n, H, n, c), dtype=torch.int8, device=dev)
     bwd_events = (ctypes.c_void_p * 4)()
     lib.tri_attn_bwd_profiled.argtypes = list(lib.tri_attn_bwd.argtypes) + [ctypes.c_void_p]
     lib.tri_attn_bwd_profiled.restype = ctypes.c_int
 
-    def step(ending: int, ev=None):
+    def step(ending: int, ev=None, rc: bool = False):
         if ev is not None:
             hip.record(ev[0], stream)
+        if rc:  # residual-compensated pair (tri_attn_fwd_rc / tri_attn_bwd_rc)
+            st = lib.tri_attn_fwd_rc(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
+                                     P(xd["gate"]), None, P(out), P(attn), P(attn_res), P(lse), P(fws),
+                                     ctypes.c_size_t(fws_bytes), stream)
+            assert st == 0, st
+            st = lib.tri_attn_bwd_rc(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
+                                     P(xd["gate"]), None, P(attn), P(attn_res), P(lse), P(xd["dout"]), P(dq), P(dk),
+                                     P(dv), P(dbias), P(dgate), P(ws), ctypes.c_size_t(ws_bytes), stream)
+            assert st == 0, st
+            return
         st = lib.tri_attn_fwd(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
                               P(xd["gate"]), None, P(out), P(attn), P(lse), P(fws), ctypes.c_size_t(fws_bytes), stream)
         assert st == 0, st
@@ -303,6 +315,20 @@ def main():
     if not args.no_end:
         end_ms, _ = timed(1, max(3, args.steps // 2), 2)
 
+    rc_ms = None
+    if not args.no_rc:
+        rc_steps = max(3, args.steps // 2)
+        for _ in range(2):
+            step(0, rc=True)
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, stream)
+        for _ in range(rc_steps):
+            step(0, rc=True)
+        hip.record(t1, stream)
+        torch.cuda.synchronize()
+        rc_ms = hip.ms(t0, t1) / rc_steps
+
     block = None if args.no_block else time_block(lib, hip, dev, stream, n, max(3, args.steps // 2), 2, args.no_end)
 
     cpu = None
@@ -318,6 +344,7 @@ def main():
         "pct_of_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
         "end_node_ms_per_step": None if end_ms is None else round(end_ms, 4),
+        "residual_compensated_ms_per_step": None if rc_ms is None else round(rc_ms, 4),
         "roofline": roofline,
         "block": block,
         "cpu_baseline": cpu,

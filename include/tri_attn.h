@@ -103,7 +103,8 @@ size_t tri_attn_fwd_workspace_size(int n_rows, int n, int h, int c, int dtype);
  *   attn_saved  pre-gate attention a, kept for the backward.
  *   lse         log-sum-exp per logit row, kept for the backward.
  *   workspace   device scratch of at least tri_attn_fwd_workspace_size bytes,
- *               256-byte aligned (holds the scaled bias tiles of this call).
+ *               256-byte aligned (holds the bias tiles of this call in the
+ *               order the kernel reads them).
  */
 int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending,
                  const void *q, const void *k, const void *v, const void *bias,
@@ -136,7 +137,7 @@ int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending,
 /*
  * tri_attn_bwd with per-stage timing: identical arguments and results, plus
  * stage_events, an array of 4 caller-created HIP events recorded on `stream`
- * before the preprocessing kernels (gate gradient, D, scaled bias), before the
+ * before the preprocessing kernels (gate gradient, D, bias tiles), before the
  * main backward kernel, before the pair-bias reduction and after it.  All four must be non-NULL
  * (TRI_ATTN_EINVAL otherwise).  Intended for benchmarks that need the main
  * kernel's own duration.
@@ -148,6 +149,43 @@ int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending
                           void *dq, void *dk, void *dv, void *dbias, void *dgate,
                           void *workspace, size_t workspace_bytes, tri_attn_stream_t stream,
                           tri_attn_event_t *stage_events);
+
+/* ------------------------------------------------------------------------
+ * Rounding-residual compensation of the saved attention (bf16 only).
+ *
+ * The pages report that saving an approximation of the fp32 -> bf16 rounding
+ * residual and using it in the backward, without changing the bf16 output,
+ * lowers the error of the query, key and pair-bias gradients (TurboPairFormer
+ * news item, "Accuratezza e riproducibilità").  Here the residual is that of
+ * attn_saved: the forward writes, besides ab = bf16(a), one int8 code per
+ * element,
+ *
+ *   code = clamp(round(256 * (a - ab) / u), -127, 127),   u = 2^(e - 134),
+ *
+ * where a is the fp32 attention value and e the biased exponent field of ab
+ * (e = 1 for zero and subnormal ab; the code is 0 when ab is inf or NaN).
+ * ab + code * u / 256 then equals a to within u / 512.  The backward
+ * preprocessing uses that value for a in D = sum_c dA * a and in the gate
+ * gradient; dq, dk and dbias depend on D, dv does not.
+ *
+ * attn_residual: int8 [n_rows][h][n][c], 16-byte aligned, written by
+ * tri_attn_fwd_rc and passed unchanged to tri_attn_bwd_rc.  All other
+ * arguments, results and errors are those of tri_attn_fwd / tri_attn_bwd;
+ * dtype must be TRI_ATTN_BF16 and attn_residual non-NULL (TRI_ATTN_EINVAL
+ * otherwise).
+ * ------------------------------------------------------------------------ */
+int tri_attn_fwd_rc(int n_rows, int n, int h, int c, int dtype, int ending,
+                    const void *q, const void *k, const void *v, const void *bias,
+                    const void *gate, const uint8_t *mask,
+                    void *out, void *attn_saved, int8_t *attn_residual, float *lse,
+                    void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
+
+int tri_attn_bwd_rc(int n_rows, int n, int h, int c, int dtype, int ending,
+                    const void *q, const void *k, const void *v, const void *bias,
+                    const void *gate, const uint8_t *mask,
+                    const void *attn_saved, const int8_t *attn_residual, const float *lse,
+                    const void *dout, void *dq, void *dk, void *dv, void *dbias, void *dgate,
+                    void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * The block around the attention: LayerNorm + projection front end and the

@@ -182,3 +182,33 @@ def test_block_validation(lib):
     assert call_out_proj_bwd(lib, ws=ctypes.c_void_p(0)) == EWORKSPACE
     assert lib.tri_attn_out_proj_bwd_workspace_size(64, 128, 128, ta.BF16) > 0
     assert lib.tri_attn_ln_proj_bwd_workspace_size(8, 8, 128, 4, 32, ta.F32) == 0
+
+
+def call_fwd_rc(lib, dtype=ta.BF16, res=None, n_rows=8, ptrs=None):
+    p = ptrs or [fake_ptr()] * 8
+    ws_bytes = lib.tri_attn_fwd_workspace_size(8, 8, 2, 32, ta.BF16)
+    return lib.tri_attn_fwd_rc(n_rows, 8, 2, 32, dtype, 0, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], res, p[7],
+                               fake_ptr(0x100000), ctypes.c_size_t(ws_bytes), None)
+
+
+def call_bwd_rc(lib, dtype=ta.BF16, res=None, n_rows=8, ptrs=None):
+    p = ptrs or [fake_ptr()] * 13
+    ws_bytes = lib.tri_attn_bwd_workspace_size(8, 8, 2, 32, ta.BF16)
+    return lib.tri_attn_bwd_rc(n_rows, 8, 2, 32, dtype, 0, p[0], p[1], p[2], p[3], p[4], None, p[5], res, p[6],
+                               p[7], p[8], p[9], p[10], p[11], p[12], fake_ptr(0x100000), ctypes.c_size_t(ws_bytes),
+                               None)
+
+
+@pytest.mark.parametrize("call,nptr", [(call_fwd_rc, 8), (call_bwd_rc, 13)])
+def test_residual_entry_validation(lib, call, nptr):
+    """The residual-compensated pair: bf16 only, residual buffer required and 16-byte aligned; the other
+    arguments are checked as for tri_attn_fwd / tri_attn_bwd (no call here reaches a launch)."""
+    good = fake_ptr(0x200000)
+    assert call(lib, dtype=ta.F32, res=good) == EINVAL
+    assert call(lib, res=None) == EINVAL
+    assert call(lib, res=fake_ptr(0x200000 + 8)) == EINVAL
+    assert call(lib, res=good, n_rows=0) == EINVAL
+    for i in range(nptr):
+        ptrs = [fake_ptr()] * nptr
+        ptrs[i] = None
+        assert call(lib, res=good, ptrs=ptrs) == EINVAL, f"null pointer {i}"

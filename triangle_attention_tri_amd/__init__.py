@@ -55,6 +55,10 @@ def load():
     lib.tri_attn_bwd_workspace_size.restype = sz
     lib.tri_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
     lib.tri_attn_bwd.restype = i
+    lib.tri_attn_fwd_rc.argtypes = [i, i, i, i, i, i] + [vp] * 11 + [sz, vp]
+    lib.tri_attn_fwd_rc.restype = i
+    lib.tri_attn_bwd_rc.argtypes = [i, i, i, i, i, i] + [vp] * 15 + [vp, sz, vp]
+    lib.tri_attn_bwd_rc.restype = i
     f = ctypes.c_float
     lib.tri_attn_ln_proj_fwd.argtypes = [i] * 6 + [vp, vp, vp, f] + [vp] * 9 + [vp]
     lib.tri_attn_ln_proj_fwd.restype = i
@@ -129,8 +133,10 @@ def fwd_workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:
     return int(load().tri_attn_fwd_workspace_size(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
 
 
-def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None):
-    """Forward.  Returns (out, attn, lse)."""
+def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None, residual: bool = False):
+    """Forward.  Returns (out, attn, lse), or (out, attn, lse, attn_residual) with
+    ``residual=True`` (bf16 only: int8 rounding-residual codes of attn, through
+    tri_attn_fwd_rc)."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -149,6 +155,13 @@ def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None):
     out = torch.empty_like(gate)
     attn = torch.empty((n_rows, h, n, c), dtype=q.dtype, device=q.device)
     lse = torch.empty((n_rows, h, n), dtype=torch.float32, device=q.device)
+    if residual:
+        res = torch.empty((n_rows, h, n, c), dtype=torch.int8, device=q.device)
+        st = lib.tri_attn_fwd_rc(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                 _ptr(gate), _ptr(mask), _ptr(out), _ptr(attn), _ptr(res), _ptr(lse),
+                                 _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(q.device))
+        _check(st, "tri_attn_fwd_rc")
+        return out, attn, lse, res
     st = lib.tri_attn_fwd(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
                           _ptr(gate), _ptr(mask), _ptr(out), _ptr(attn), _ptr(lse), _ptr(workspace),
                           ctypes.c_size_t(workspace.numel()), _stream(q.device))
@@ -156,8 +169,9 @@ def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None):
     return out, attn, lse
 
 
-def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, workspace=None):
-    """Backward.  Returns (dq, dk, dv, dbias, dgate)."""
+def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, workspace=None, attn_residual=None):
+    """Backward.  Returns (dq, dk, dv, dbias, dgate).  ``attn_residual`` (the
+    codes from ``fwd(..., residual=True)``) selects tri_attn_bwd_rc."""
     import torch
     lib = load()
     dt = _dtype_code(q)
@@ -172,6 +186,15 @@ def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, worksp
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dbias, dgate = torch.empty_like(bias), torch.empty_like(gate)
+    if attn_residual is not None:
+        if attn_residual.dtype != torch.int8 or attn_residual.device != q.device or not attn_residual.is_contiguous():
+            raise TypeError("attn_residual must be a contiguous int8 tensor on the same device")
+        st = lib.tri_attn_bwd_rc(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
+                                 _ptr(gate), _ptr(mask), _ptr(attn), _ptr(attn_residual), _ptr(lse), _ptr(dout),
+                                 _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dbias), _ptr(dgate), _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel()), _stream(q.device))
+        _check(st, "tri_attn_bwd_rc")
+        return dq, dk, dv, dbias, dgate
     st = lib.tri_attn_bwd(n_rows, n, h, c, dt, int(bool(ending)), _ptr(q), _ptr(k), _ptr(v), _ptr(bias),
                           _ptr(gate), _ptr(mask), _ptr(attn), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                           _ptr(dv), _ptr(dbias), _ptr(dgate), _ptr(workspace), ctypes.c_size_t(workspace.numel()),

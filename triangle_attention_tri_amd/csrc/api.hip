@@ -128,7 +128,7 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
     L.rows = 1;
     L.nsplit = pick_nsplit(dtype, n);
     L.bias_prep = after_d;
-    // prepared bias: fp16 for bf16 runs, fp32 for fp32 runs (plus one zero tile)
+    // prepared bias: bf16 operand tiles for bf16 runs, fp32 for fp32 runs (plus one zero tile)
     L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * (dtype == TRI_ATTN_BF16 ? 2 : 4));
     // bf16 sums the dS tiles of each row group before storing them
     L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS : n_rows;
@@ -155,20 +155,22 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_E
 
 template <typename T>
 int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const void* bias, const void* gate,
-           const uint8_t* mask, void* out, void* attn, float* lse, void* ws, hipStream_t st) {
+           const uint8_t* mask, void* out, void* attn, int8_t* attn_res, float* lse, void* ws, hipStream_t st) {
   FwdArgs<T> a;
   a.geo = geo;
   a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v;
   a.bias = (const T*)bias; a.gate = (const T*)gate; a.mask = mask;
   a.out = (T*)out; a.attn = (T*)attn; a.lse = lse;
   a.bias_prep = (float*)ws;
+  a.attn_res = attn_res;
   return hip_status(launch_fwd<T, FWD_R>(a, st));
 }
 
 template <typename T>
 int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, const void* v, const void* bias,
-           const void* gate, const uint8_t* mask, const void* attn, const float* lse, const void* dout,
-           void* dq, void* dk, void* dv, void* dbias, void* dgate, void* ws, hipStream_t st, hipEvent_t* ev) {
+           const void* gate, const uint8_t* mask, const void* attn, const int8_t* attn_res, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate, void* ws, hipStream_t st,
+           hipEvent_t* ev) {
   BwdArgs<T> a;
   a.geo = geo;
   a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v; a.bias = (const T*)bias;
@@ -185,6 +187,8 @@ int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, cons
   a.dq_part = base + L.dq_part;
   a.trash = (float*)(base + L.trash);
   a.nsplit = L.nsplit;
+  a.attn_res = attn_res;
+  if (attn_res != nullptr && L.kpw == 0) return TRI_ATTN_EUNSUPPORTED;  // only the tiled kernels' preprocess reads it
   hipError_t e;
   if (L.kpw > 0) {
     a.slab_rows = L.slab_rows;
@@ -234,9 +238,10 @@ size_t tri_attn_fwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
   return align256(fwd_workspace_bytes(n, h));
 }
 
-int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
-                 const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
-                 void* attn_saved, float* lse, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+static int fwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                    const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
+                    void* attn_saved, int8_t* attn_res, float* lse, void* workspace, size_t workspace_bytes,
+                    hipStream_t s) {
   int st = check_common(n_rows, n, h, c, dtype, ending);
   if (st != TRI_ATTN_OK) return st;
   const void* req[] = {q, k, v, bias, gate, out, attn_saved, lse};
@@ -245,10 +250,25 @@ int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const v
   if (workspace == nullptr || workspace_bytes < align256(fwd_workspace_bytes(n, h))) return TRI_ATTN_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
   const Geo geo = make_geo(n_rows, n, h, ending);
-  hipStream_t s = (hipStream_t)stream;
   if (dtype == TRI_ATTN_BF16)
-    return do_fwd<bf16>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, workspace, s);
-  return do_fwd<float>(geo, q, k, v, bias, gate, mask, out, attn_saved, lse, workspace, s);
+    return do_fwd<bf16>(geo, q, k, v, bias, gate, mask, out, attn_saved, attn_res, lse, workspace, s);
+  return do_fwd<float>(geo, q, k, v, bias, gate, mask, out, attn_saved, nullptr, lse, workspace, s);
+}
+
+int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                 const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
+                 void* attn_saved, float* lse, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  return fwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, out, attn_saved, nullptr, lse,
+                  workspace, workspace_bytes, (hipStream_t)stream);
+}
+
+int tri_attn_fwd_rc(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                    const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
+                    void* attn_saved, int8_t* attn_residual, float* lse, void* workspace, size_t workspace_bytes,
+                    tri_attn_stream_t stream) {
+  if (dtype != TRI_ATTN_BF16 || attn_residual == nullptr || !aligned16(attn_residual)) return TRI_ATTN_EINVAL;
+  return fwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, out, attn_saved, attn_residual, lse,
+                  workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
@@ -258,8 +278,9 @@ size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
 
 static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
                     const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
-                    const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate,
-                    void* workspace, size_t workspace_bytes, hipStream_t s, hipEvent_t* ev) {
+                    const int8_t* attn_res, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* dbias, void* dgate, void* workspace, size_t workspace_bytes, hipStream_t s,
+                    hipEvent_t* ev) {
   int st = check_common(n_rows, n, h, c, dtype, ending);
   if (st != TRI_ATTN_OK) return st;
   const void* req[] = {q, k, v, bias, gate, attn_saved, lse, dout, dq, dk, dv, dbias, dgate};
@@ -271,9 +292,9 @@ static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, cons
   if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
   const Geo geo = make_geo(n_rows, n, h, ending);
   if (dtype == TRI_ATTN_BF16)
-    return do_bwd<bf16>(geo, L, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv, dbias, dgate,
-                        workspace, s, ev);
-  return do_bwd<float>(geo, L, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv, dbias, dgate,
+    return do_bwd<bf16>(geo, L, q, k, v, bias, gate, mask, attn_saved, attn_res, lse, dout, dq, dk, dv, dbias,
+                        dgate, workspace, s, ev);
+  return do_bwd<float>(geo, L, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk, dv, dbias, dgate,
                        workspace, s, ev);
 }
 
@@ -281,8 +302,17 @@ int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending, const v
                  const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate,
                  void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
-  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv,
-                  dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk,
+                  dv, dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
+}
+
+int tri_attn_bwd_rc(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                    const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
+                    const int8_t* attn_residual, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                    void* dbias, void* dgate, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  if (dtype != TRI_ATTN_BF16 || attn_residual == nullptr || !aligned16(attn_residual)) return TRI_ATTN_EINVAL;
+  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, attn_residual, lse, dout,
+                  dq, dk, dv, dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, nullptr);
 }
 
 int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
@@ -293,8 +323,8 @@ int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending
   if (stage_events == nullptr) return TRI_ATTN_EINVAL;
   for (int i = 0; i < 4; i++)
     if (stage_events[i] == nullptr) return TRI_ATTN_EINVAL;
-  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, lse, dout, dq, dk, dv,
-                  dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, (hipEvent_t*)stage_events);
+  return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk,
+                  dv, dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, (hipEvent_t*)stage_events);
 }
 
 // ---------------------------------------------------------------------------

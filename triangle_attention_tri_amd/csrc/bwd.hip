@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdArgs<T> a) {
     const float da = dov * sg;
     a.dgate[ip + c] = from_f<T>(dov * av * sg * (1.0f - sg));
     a.dA[ia + c] = from_f<T>(da);
-    dsum += da * av;
+    dsum += to_f(from_f<T>(da)) * av;  // the dA the main kernel multiplies
   }
   a.Dsum[((long long)row * G.H + h) * G.n + j] = dsum;
 }

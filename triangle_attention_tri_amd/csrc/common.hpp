@@ -305,6 +305,7 @@ template <typename T> struct FwdArgs {
   T *out, *attn;
   float* lse;
   float* bias_prep;  // workspace: bias tiles in per-lane order (bf16 operand tiles; sqrt(c)-scaled fp32 in fp32 runs)
+  int8_t* attn_res;  // optional (bf16 runs): rounding-residual codes of attn, [n_rows][H][n][C]; null = not written
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;
@@ -343,6 +344,7 @@ template <typename T> struct BwdArgs {
   int nsplit;        // key-range splits per row in the tile kernel
   int slab_rows;     // row slabs of dS tiles the dbias reduction sums (rows, or row groups)
   int slab_e;        // slab tile layout [16 / slab_e parts][64 lanes][slab_e values]
+  const int8_t* attn_res;  // optional (bf16 runs): rounding-residual codes of attn from the forward; null = none
 };
 
 // 16 consecutive floats (64 bytes, 16-byte aligned) as one accumulator tile's
@@ -397,6 +399,35 @@ __device__ __forceinline__ Op<bf16> load_bias_op(const bf16* tile_lane) {
 // Writes the prepared bias tiles ([h][nt][nt][64][16] bf16 and one zero tile)
 // of a bf16 call into `out`, which holds (h nt^2 + 1) * 2048 bytes.
 hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStream_t st);
+
+// ---------------------------------------------------------------------------
+// Rounding-residual codes of the saved attention (bf16 runs).
+//
+// The forward keeps the pre-gate attention a in bf16; its fp32 value is
+// ab + r with ab = bf16(a) and |r| at most half the bf16 spacing u at ab
+// (u = 2^(e - 134) for the biased exponent e of ab, e = 1 for zero and
+// subnormals).  The code is round(256 r / u), clamped to [-127, 127], one
+// byte per element; decoding gives a to within u / 512, i.e. about 2^-16
+// relative instead of bf16's 2^-9.  The bf16 output itself is unchanged.
+// (Reading of the TurboPairFormer news item, "Accuratezza e riproducibilità":
+// an approximation of the fp32 -> bf16 rounding residual is saved and used by
+// the backward.)
+__device__ __forceinline__ int residual_exp(float ab) {
+  const int e = (int)((__float_as_uint(ab) >> 23) & 0xffu);
+  return e == 0 ? 1 : e;
+}
+__device__ __forceinline__ int8_t residual_code(float a, bf16 ab) {
+  const float abf = (float)ab;
+  const int e = residual_exp(abf);
+  if (e == 255) return 0;                                     // inf / nan: no residual
+  const float x = __builtin_amdgcn_ldexpf(a - abf, 142 - e);  // 256 r / u (the difference is exact)
+  return (int8_t)fminf(fmaxf(__builtin_rintf(x), -127.0f), 127.0f);
+}
+// residual value of a saved bf16 element (given as its fp32 value) from its code
+__device__ __forceinline__ float residual_value(float abf, int code) {
+  const int e = residual_exp(abf);
+  return e == 255 ? 0.0f : __builtin_amdgcn_ldexpf((float)code, e - 142);
+}
 
 // XCD-aware work order.  Workgroups are dispatched to the eight XCDs round
 // robin (workgroup b runs on XCD b % 8, each with its own L2).  This maps the

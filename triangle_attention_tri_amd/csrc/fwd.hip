@@ -317,7 +317,14 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void fwd_kernel(FwdA
         const bf16x4 gv = *reinterpret_cast<const bf16x4*>(a.gate + ig + c0);
 #pragma unroll
         for (int t = 0; t < 4; t++) ov[t] = sigmoidf_((float)gv[t]) * av[t];
-        *reinterpret_cast<bf16x4*>(a.attn + ia + c0) = (bf16x4){(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
+        const bf16x4 ab = (bf16x4){(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
+        *reinterpret_cast<bf16x4*>(a.attn + ia + c0) = ab;
+        if (a.attn_res != nullptr) {
+          uint32_t codes = 0;
+#pragma unroll
+          for (int t = 0; t < 4; t++) codes |= (uint32_t)(uint8_t)residual_code(av[t], ab[t]) << (8 * t);
+          *reinterpret_cast<uint32_t*>(a.attn_res + ia + c0) = codes;
+        }
         *reinterpret_cast<bf16x4*>(a.out + ig + c0) = (bf16x4){(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
       } else {
         const f32x4 gv = *reinterpret_cast<const f32x4*>(a.gate + ig + c0);
