@@ -1,18 +1,20 @@
-// Backward, one workgroup per (row i, head h, key range) -- the path used up to
-// n = 768 (bf16) / 256 (fp32).
+// Tiled backward kernels.
 //
-// The keys of a row are split into nsplit contiguous ranges of at most eight
-// 32-key tiles, so that each of the four waves owns at most two of them and two
-// workgroups fit on a CU.  A wave
-// keeps the V operands of its tiles and their dK / dV accumulators in
-// registers for the whole row, so dK and dV are complete when the row ends and
-// are written once.  K of the key range sits in LDS (read as the logit operand
-// and, transposed, as the dQ operand).  Query tiles are walked in order; the
-// next tile's Q and dA rows and its log-sum-exp / D values are loaded into
-// registers while the current one is computed, then written to the other half
-// of a double-buffered LDS area.  For every (query tile, key tile) the logit
-// tile S = Q K^T + b and P = exp(S - lse) are recomputed ONCE and feed all
-// four gradients (TurboPairFormer news item, "Dove si impiega il tempo"):
+// bf16 runs use bwd_group_kernel (four rows per workgroup, described where it
+// is defined).  fp32 runs up to n = 256 use bwd_tile_kernel, one workgroup
+// per (row i, head h), instantiated for fp32 only:
+//
+// The row's keys form one range of at most eight 32-key tiles, so that each of
+// the four waves owns at most two of them.  A wave keeps the V operands of its
+// tiles and their dK / dV accumulators in registers for the whole row, so dK
+// and dV are complete when the row ends and are written once.  K of the key
+// range sits in LDS (read as the logit operand and, transposed, as the dQ
+// operand).  Query tiles are walked in order; the next tile's Q and dA rows
+// and its log-sum-exp / D values are loaded into registers while the current
+// one is computed, then written to the other half of a double-buffered LDS
+// area.  For every (query tile, key tile) the logit tile S = Q K^T + b and
+// P = exp(S - lse) are recomputed ONCE and feed all four gradients
+// (TurboPairFormer news item, "Dove si impiega il tempo"):
 //     dP - D = dA V^T - D     (D folded into the MFMA accumulator input)
 //     dS     = P (dP - D)
 //     dV^T  += dA^T P,   dK^T += Q^T dS,   dQ += dS K,   dbias partial = dS.
@@ -20,13 +22,10 @@
 // and dK products straight from the accumulator; dA^T and Q^T come from the
 // LDS copies through the gfx950 transposing read, and dS goes through a small
 // per-wave LDS tile to become the row operand of dQ.  dQ of a query tile is
-// the sum of the four waves' partials, added in wave order after a barrier;
-// with two key ranges each range writes an fp32 partial and a later kernel
-// adds the two in range order.
+// the sum of the four waves' partials, added in wave order after a barrier.
 // The pair-bias gradient needs a sum over rows i, which no workgroup owns: each
-// row writes its dS tiles (in the operand precision T, as they enter the dQ
-// and dK products) and a separate kernel sums them over rows in ascending
-// order in fp32.
+// row writes its dS tiles and a separate kernel sums them over rows in
+// ascending order in fp32.
 // A row whose keys are all masked has uniform weights 1/n and no gradient
 // through its logits: it takes a separate short path (dV = mean of dA over the
 // queries, dQ = dK = 0, zero dS tiles) and never enters the tile loop.
@@ -1036,11 +1035,8 @@ hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* 
 template hipError_t launch_bwd_group<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_group<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 
-template hipError_t launch_bwd_tile<bf16, 1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<bf16, 2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<float, 1>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
 template hipError_t launch_bwd_tile<float, 2>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
-template size_t tile_smem<bf16>(int);
 template size_t tile_smem<float>(int);
 
 }  // namespace tri
