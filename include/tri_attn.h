@@ -138,7 +138,9 @@ int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending,
  * tri_attn_bwd with per-stage timing: identical arguments and results, plus
  * stage_events, an array of 4 caller-created HIP events recorded on `stream`
  * before the preprocessing kernels (gate gradient, D, bias tiles), before the
- * main backward kernel, before the pair-bias reduction and after it.  All four must be non-NULL
+ * main backward kernel, before the pair-bias reduction and after it.  A NULL
+ * entry is not recorded (each record puts a few microseconds of idle time
+ * between the kernels it separates); the array itself must be non-NULL
  * (TRI_ATTN_EINVAL otherwise).  Intended for benchmarks that need the main
  * kernel's own duration.
  */

@@ -321,8 +321,6 @@ int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending
                           void* dbias, void* dgate, void* workspace, size_t workspace_bytes,
                           tri_attn_stream_t stream, tri_attn_event_t* stage_events) {
   if (stage_events == nullptr) return TRI_ATTN_EINVAL;
-  for (int i = 0; i < 4; i++)
-    if (stage_events[i] == nullptr) return TRI_ATTN_EINVAL;
   return bwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk,
                   dv, dbias, dgate, workspace, workspace_bytes, (hipStream_t)stream, (hipEvent_t*)stage_events);
 }

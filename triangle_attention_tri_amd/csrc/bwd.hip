@@ -297,11 +297,11 @@ hipError_t launch_bwd(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
   const Geo& G = a.geo;
   const long long pre_total = (long long)G.n_rows * G.n * G.H;
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_pre_kernel<T>), dim3((unsigned)((pre_total + 255) / 256)), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   const size_t smem = BwdSmem<T, R>::total(G.n);
   static bool attr_set = false;
   if (!attr_set) {
@@ -313,12 +313,12 @@ hipError_t launch_bwd(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
   hipLaunchKernelGGL((bwd_main_kernel<T, R>), dim3(a.groups, G.H), dim3(256), smem, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if (ev && ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_total = (long long)G.H * G.n * G.n;
   hipLaunchKernelGGL((dbias_reduce_kernel<T>), dim3((unsigned)((red_total + 255) / 256)), dim3(256), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  if (ev && ev[3] && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 

@@ -959,7 +959,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   const Geo& G = a.geo;
   const int nt = (G.n + TILE - 1) / TILE;
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   const int pre_threads = G.n * G.H * 4;  // per row
   hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
                      dim3(256), 0, st, a);
@@ -968,7 +968,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
                      G, a.bias, a.bias_prep);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;
   if (!attr_set) {
     e = hipFuncSetAttribute((const void*)bwd_tile_kernel<T, KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -979,7 +979,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
   hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(a.nsplit * G.n_rows * G.H), dim3(256), TileSmem<T>::total(KPW),
                      st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if (ev && ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_threads = (long long)G.H * nt * nt * 128;
   hipLaunchKernelGGL((dbias_tile_reduce_kernel<T>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -988,7 +988,7 @@ hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) 
     hipLaunchKernelGGL((dq_sum_kernel<T>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  if (ev && ev[3] && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
@@ -1000,13 +1000,13 @@ hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* 
   const Geo& G = a.geo;
   const int nt = (G.n + TILE - 1) / TILE;
   hipError_t e;
-  if (ev && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
+  if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   const int pre_threads = G.n * G.H * 4;  // per row
   hipLaunchKernelGGL((bwd_pre_vec_kernel<bf16>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
                      dim3(256), 0, st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st)) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   static bool attr_set = false;
   if (!attr_set) {
     e = hipFuncSetAttribute((const void*)bwd_group_kernel<BF16_GROUP_ROWS, KPW>,
@@ -1018,7 +1018,7 @@ hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* 
   hipLaunchKernelGGL((bwd_group_kernel<BF16_GROUP_ROWS, KPW>), dim3(a.nsplit * ngroups * G.H), dim3(512),
                      GroupSmem<BF16_GROUP_ROWS>::total(KPW), st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
+  if (ev && ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
   const long long red_threads = (long long)G.H * nt * nt * 128;
   hipLaunchKernelGGL((dbias_tile_reduce_kernel<bf16>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st,
                      a);
@@ -1028,7 +1028,7 @@ hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* 
     hipLaunchKernelGGL((dq_sum_kernel<bf16>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (ev && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
+  if (ev && ev[3] && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
