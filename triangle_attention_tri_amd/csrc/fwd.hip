@@ -1,11 +1,11 @@
 // Forward: logits + pair bias + mask, online softmax, P.V, sigmoid gate.
 //
 // Work split.  A workgroup of four waves takes R consecutive rows i of one head
-// h and 128 consecutive queries j (32 per wave); two workgroups share a CU.  It
-// walks the keys in tiles of 32.  The K and V rows of the next tile are loaded
-// from HBM into registers while the current tile is computed, then written to
-// the other half of a double-buffered LDS area, so there is one barrier per
-// key tile.  The logit tile is computed transposed (keys x queries): each lane
+// h and 128 consecutive queries j (32 per wave); three workgroups share a CU
+// in bf16 runs (168 VGPRs), two in fp32 runs.  It walks the keys in tiles of
+// 32.  The K and V rows of the next tile are loaded from HBM into registers
+// while the current tile is computed, then written to the other half of a
+// double-buffered LDS area, so there is one barrier per key tile.  The logit tile is computed transposed (keys x queries): each lane
 // owns one query and 16 of the tile's keys, the other lane half owns the other
 // 16.  The pair-bias term is the logit MFMA's accumulator input, shared by the
 // R rows (the bias does not depend on i).  In bf16 runs two MFMAs form it per
