@@ -301,3 +301,51 @@ def test_autograd_function(device):
     assert_close("autograd out", out.detach().cpu(), ref["out"], 2e-2)
     for name, key in (("q", "dq"), ("k", "dk"), ("v", "dv"), ("bias", "dbias"), ("gate", "dgate")):
         assert_close(f"autograd {key}", leaves[name].grad.cpu(), ref[key], 2e-2)
+
+
+def test_large_bias(device):
+    """bf16 with a wide pair bias (std 30, |b| up to ~130): the bias term enters through MFMAs with
+    sqrt(c) held in bf16 (relative error 1.1e-4 of the term), still inside the bf16 bar."""
+    n = 96
+    xc = inputs.attn_inputs(n, 4, 32, torch.bfloat16, seed=5, bias_std=30.0)
+    log(f"large bias n={n}: max |b| = {xc['bias'].float().abs().max().item():.1f}")
+    res = run_gpu(to_dev(xc, device))
+    check_full("bias_std30", xc, res, TOL[torch.bfloat16])
+
+
+def test_profiled_stage_events(device):
+    """tri_attn_bwd_profiled with some stage events NULL gives tri_attn_bwd's results bit for bit and
+    times the stages it was given events for."""
+    import ctypes
+    n = 128
+    xc = inputs.attn_inputs(n, 4, 32, torch.bfloat16, seed=3)
+    x = to_dev(xc, device)
+    out, attn, lse = ta.fwd(x["q"], x["k"], x["v"], x["bias"], x["gate"], None)
+    ref = ta.bwd(x["q"], x["k"], x["v"], x["bias"], x["gate"], None, attn, lse, x["dout"])
+    lib = ta.load()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    ev = [ctypes.c_void_p() for _ in range(2)]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    stage = (ctypes.c_void_p * 4)(None, ev[0], ev[1], None)
+    ws = torch.empty(ta.workspace_size(n, n, 4, 32, torch.bfloat16), dtype=torch.uint8, device=device)
+    outs = [torch.empty_like(t) for t in ref]
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    lib.tri_attn_bwd_profiled.argtypes = list(lib.tri_attn_bwd.argtypes) + [ctypes.c_void_p]
+    lib.tri_attn_bwd_profiled.restype = ctypes.c_int
+    stream = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    st = lib.tri_attn_bwd_profiled(n, n, 4, 32, ta.BF16, 0, P(x["q"]), P(x["k"]), P(x["v"]), P(x["bias"]),
+                                   P(x["gate"]), None, P(attn), P(lse), P(x["dout"]), *[P(t) for t in outs], P(ws),
+                                   ctypes.c_size_t(ws.numel()), stream, ctypes.cast(stage, ctypes.c_void_p))
+    assert st == 0, st
+    torch.cuda.synchronize()
+    for a, b in zip(outs, ref):
+        assert torch.equal(a, b)
+    ms = ctypes.c_float()
+    assert hip.hipEventSynchronize(ev[1]) == 0
+    assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+    log(f"main backward kernel at n={n}: {ms.value:.3f} ms")
+    assert ms.value > 0.0

@@ -72,3 +72,23 @@ def test_residual_compensation(device, widx):
     assert gains["dgate"] > 0.10
     for k in ("dq", "dk", "dbias"):
         assert gains[k] >= 0.0, f"{k}: compensated mean error above the plain one"
+
+
+def test_residual_ending_node_masked(device):
+    """The compensated pair at the ending node with a mask that drops a whole row: same bar as the
+    plain pair, dv and the forward outputs unchanged."""
+    from tests.test_gpu_parity import check_full, TOL
+    n = 45
+    xc = inputs.attn_inputs(n, 4, 32, torch.bfloat16, seed=7, bias_std=2.0)
+    xc["mask"] = inputs.random_mask(n, seed=9, p_keep=0.8, full_rows=(4,))
+    x = to_dev(xc, device)
+    args = (x["q"], x["k"], x["v"], x["bias"], x["gate"], x["mask"])
+    out, attn, lse, res = ta.fwd(*args, ending=True, residual=True)
+    out0, attn0, lse0 = ta.fwd(*args, ending=True)
+    assert torch.equal(out, out0) and torch.equal(attn, attn0) and torch.equal(lse, lse0)
+    g0 = ta.bwd(*args, attn0, lse0, x["dout"], ending=True)
+    g1 = ta.bwd(*args, attn, lse, x["dout"], ending=True, attn_residual=res)
+    torch.cuda.synchronize()
+    assert torch.equal(g1[2], g0[2])
+    got = dict(out=out, attn=attn, lse=lse, dq=g1[0], dk=g1[1], dv=g1[2], dbias=g1[3], dgate=g1[4])
+    check_full(f"rc_end{n}", xc, got, TOL[torch.bfloat16], ending=True)
