@@ -204,6 +204,43 @@ def time_block(lib, hip, dev, stream, n, steps, warmup, no_end):
     }
 
 
+def time_chunked(lib, hip, dev, stream, n, steps, warmup, rows_list=(768, 128, 32)):
+    """Chunked inference of the starting-node block (tri_attn_block_fwd_chunked) at several chunk sizes:
+    forward time per call and the workspace it needs, next to the unchunked forward's intermediates."""
+    import torch
+
+    import triangle_attention_tri_amd as ta
+    from triangle_attention_tri_amd import inputs
+    H, c, cz = 4, 32, 128
+    x = {k: v.to(dev) for k, v in inputs.block_inputs(n, cz=cz, h=H, c=c, seed=4).items()}
+    y = torch.empty_like(x["z"])
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    res = []
+    for rows in rows_list:
+        rows = min(rows, n)
+        need = lib.tri_attn_block_fwd_chunked_workspace_size(n, cz, H, c, ta.BF16, rows)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+
+        def call():
+            st = lib.tri_attn_block_fwd_chunked(n, cz, H, c, ta.BF16, rows, P(x["z"]), P(x["gamma"]), P(x["beta"]),
+                                                ctypes.c_float(1e-5), P(x["w_qkvg"]), P(x["w_bias"]), P(x["w_o"]),
+                                                None, P(y), P(ws), ctypes.c_size_t(need), stream)
+            assert st == 0, st
+        for _ in range(warmup):
+            call()
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, stream)
+        for _ in range(steps):
+            call()
+        hip.record(t1, stream)
+        torch.cuda.synchronize()
+        res.append({"rows_per_chunk": rows, "ms": round(hip.ms(t0, t1) / steps, 4),
+                    "workspace_mib": round(need / 2 ** 20, 1)})
+        del ws
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +250,7 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
     ap.add_argument("--no-rc", action="store_true", help="skip the timing of the residual-compensated pair")
+    ap.add_argument("--no-chunked", action="store_true", help="skip the chunked block inference timing")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the LayerNorm + projection + attention + output-linear block timing")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -353,6 +391,7 @@ def main():
         rc_ms = hip.ms(t0, t1) / rc_steps
 
     block = None if args.no_block else time_block(lib, hip, dev, stream, n, max(3, args.steps // 2), 2, args.no_end)
+    chunked = None if args.no_chunked else time_chunked(lib, hip, dev, stream, n, 3, 1)
 
     cpu = None
     if rank == 0 and args.cpu_rows > 0:
@@ -370,6 +409,7 @@ def main():
         "residual_compensated_ms_per_step": None if rc_ms is None else round(rc_ms, 4),
         "roofline": roofline,
         "block": block,
+        "chunked_block_fwd": chunked,
         "cpu_baseline": cpu,
     }
     if rank == 0:

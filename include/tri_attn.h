@@ -260,6 +260,42 @@ int tri_attn_out_proj_bwd(int n_pairs, int c_in, int c_out, int dtype,
                           void *dx, void *dw, void *workspace, size_t workspace_bytes,
                           tri_attn_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Chunked inference of the starting-node block (forward only).  The FastFold
+ * review ("提出的方法", "主要发现") describes memory-aware chunking for
+ * inference, chosen automatically from the memory available.  Every step of
+ * the block acts on one pair row i at a time except the pair bias, which each
+ * row reads whole.  So the block can run over chunks of rows_per_chunk pair
+ * rows, with only the bias and one chunk's intermediates resident:
+ *
+ *   pass 1, each chunk: LayerNorm + projections, keeping the bias rows;
+ *   pass 2, each chunk: LayerNorm + projections again, attention over the full
+ *   bias, output linear into the chunk's rows of y.
+ *
+ * y is bit for bit the y of the unchunked block
+ * (tri_attn_ln_proj_fwd -> tri_attn_fwd -> tri_attn_out_proj_fwd) for every
+ * rows_per_chunk; the projections are computed twice.  Sizes and dtypes are
+ * those of the block calls (bf16, c_z = 128, h*c = 128); z, y [n][n][c_z]; mask
+ * [n][n] or NULL; 1 <= rows_per_chunk <= n (TRI_ATTN_EINVAL otherwise).
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace for one rows_per_chunk (0 on bad args): the full
+ * bias, one chunk's projections, attention outputs and statistics, and the
+ * attention forward's workspace. */
+size_t tri_attn_block_fwd_chunked_workspace_size(int n, int cz, int h, int c, int dtype, int rows_per_chunk);
+
+/* The largest rows_per_chunk whose workspace fits in workspace_budget bytes,
+ * or 0 when even one row does not fit (or the arguments are invalid). */
+int tri_attn_block_chunk_rows(int n, int cz, int h, int c, int dtype, size_t workspace_budget);
+
+/* The chunked forward: writes y.  workspace: 256-byte aligned, at least
+ * tri_attn_block_fwd_chunked_workspace_size bytes, contents on entry ignored. */
+int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_per_chunk,
+                               const void *z, const void *ln_gamma, const void *ln_beta, float ln_eps,
+                               const void *w_qkvg, const void *w_bias, const void *w_o,
+                               const uint8_t *mask, void *y,
+                               void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

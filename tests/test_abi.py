@@ -212,3 +212,35 @@ def test_residual_entry_validation(lib, call, nptr):
         ptrs = [fake_ptr()] * nptr
         ptrs[i] = None
         assert call(lib, res=good, ptrs=ptrs) == EINVAL, f"null pointer {i}"
+
+
+def test_chunked_block_contract(lib):
+    """Workspace sizes and the budget -> chunk choice of the chunked block forward, and its argument checks
+    (none of these calls reaches a launch)."""
+    n, cz, h, c = 64, 128, 4, 32
+    size = lambda r: lib.tri_attn_block_fwd_chunked_workspace_size(n, cz, h, c, ta.BF16, r)  # noqa: E731
+    sizes = [size(r) for r in range(1, n + 1)]
+    assert all(s > 0 and s % 256 == 0 for s in sizes)
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    assert size(0) == 0 and size(n + 1) == 0
+    assert lib.tri_attn_block_fwd_chunked_workspace_size(n, cz, h, c, ta.F32, 8) == 0
+    assert lib.tri_attn_block_fwd_chunked_workspace_size(n, 64, h, c, ta.BF16, 8) == 0
+    # at least the full bias and one row of the four projections
+    assert sizes[0] >= h * n * n * 2 + 4 * n * h * c * 2
+    for r in (1, 7, 32, n):
+        assert lib.tri_attn_block_chunk_rows(n, cz, h, c, ta.BF16, ctypes.c_size_t(size(r))) == r
+        assert lib.tri_attn_block_chunk_rows(n, cz, h, c, ta.BF16, ctypes.c_size_t(size(r) + 255)) == r
+    assert lib.tri_attn_block_chunk_rows(n, cz, h, c, ta.BF16, ctypes.c_size_t(size(1) - 1)) == 0
+    assert lib.tri_attn_block_chunk_rows(n, cz, h, c, ta.BF16, ctypes.c_size_t(1 << 40)) == n
+
+    def call(rows=8, y=fake_ptr(), ws_bytes=None, eps=1e-5):
+        need = size(8) if ws_bytes is None else ws_bytes
+        return lib.tri_attn_block_fwd_chunked(n, cz, h, c, ta.BF16, rows, fake_ptr(), fake_ptr(), fake_ptr(),
+                                              ctypes.c_float(eps), fake_ptr(), fake_ptr(), fake_ptr(), None, y,
+                                              fake_ptr(0x100000), ctypes.c_size_t(need), None)
+    assert call(rows=0) == EINVAL
+    assert call(rows=n + 1) == EINVAL
+    assert call(y=None) == EINVAL
+    assert call(y=fake_ptr(2)) == EINVAL
+    assert call(eps=0.0) == EINVAL
+    assert call(ws_bytes=size(8) - 1) == EWORKSPACE

@@ -136,3 +136,30 @@ def test_block_determinism(device):
     for r in runs[1:]:
         for key in runs[0]:
             assert torch.equal(runs[0][key], r[key]), key
+
+
+def test_block_fwd_chunked(device):
+    """Chunked inference of the starting-node block: y is bit for bit the unchunked block's for chunks that
+    divide n, do not divide it and are single rows, and matches the block oracle; a budget picks the largest
+    chunk whose workspace fits."""
+    n = 96
+    x = inputs.block_inputs(n, seed=51, affine=True)
+    x["mask"] = inputs.random_mask(n, seed=52, p_keep=0.8, full_rows=(5,))
+    xd = dev(x, device)
+    w = (xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"])
+    y_full, _ = ta.block_fwd(*w, mask=xd["mask"])
+    torch.cuda.synchronize()
+    ref = B.block_fwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], x["w_o"], H, C, mask=x["mask"])
+    e = assert_close("y(unchunked)", y_full.cpu(), ref["y"], TOL)
+    log(f"chunked block n={n}: unchunked y error {e:.2e}")
+    sizes = {}
+    for rows in (n, 32, 37, 1):
+        y, r, need = ta.block_fwd_chunked(*w, mask=xd["mask"], rows_per_chunk=rows)
+        torch.cuda.synchronize()
+        assert r == rows
+        assert torch.equal(y, y_full), f"rows_per_chunk={rows}: y differs from the unchunked block"
+        sizes[rows] = need
+        log(f"  rows_per_chunk={rows}: workspace {need / 2**20:.2f} MiB, bitwise equal")
+    y, r, need = ta.block_fwd_chunked(*w, mask=xd["mask"], budget_bytes=sizes[37] + 100)
+    torch.cuda.synchronize()
+    assert r >= 37 and need <= sizes[37] + 100 and torch.equal(y, y_full)

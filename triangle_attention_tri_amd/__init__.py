@@ -72,6 +72,12 @@ def load():
     lib.tri_attn_out_proj_bwd_workspace_size.restype = sz
     lib.tri_attn_out_proj_bwd.argtypes = [i] * 4 + [vp] * 5 + [vp, sz, vp]
     lib.tri_attn_out_proj_bwd.restype = i
+    lib.tri_attn_block_fwd_chunked_workspace_size.argtypes = [i] * 6
+    lib.tri_attn_block_fwd_chunked_workspace_size.restype = sz
+    lib.tri_attn_block_chunk_rows.argtypes = [i] * 5 + [sz]
+    lib.tri_attn_block_chunk_rows.restype = i
+    lib.tri_attn_block_fwd_chunked.argtypes = [i] * 6 + [vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tri_attn_block_fwd_chunked.restype = i
     _lib = lib
     return lib
 
@@ -309,6 +315,40 @@ def block_bwd(z, gamma, beta, w_qkvg, w_bias, w_o, saved, dy, ending: bool = Fal
     dz, dgamma, dbeta, dw_qkvg, dw_bias = ln_proj_bwd(z, gamma, beta, s["mean"], s["rstd"], w_qkvg, w_bias, dq, dk,
                                                       dv, dgate, dbias)
     return dict(dz=dz, dgamma=dgamma, dbeta=dbeta, dw_qkvg=dw_qkvg, dw_bias=dw_bias, dw_o=dw_o)
+
+
+def block_fwd_chunked(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_chunk=None, budget_bytes=None,
+                      eps: float = 1e-5, h: int = 4, c: int = 32):
+    """Chunked inference of the starting-node block (tri_attn_block_fwd_chunked).
+
+    ``rows_per_chunk`` pair rows at a time, or, with ``budget_bytes``, the
+    largest chunk whose workspace fits (tri_attn_block_chunk_rows).  Returns
+    (y, rows_per_chunk, workspace_bytes).
+    """
+    import torch
+    lib = load()
+    n, n2, cz = z.shape
+    if n != n2:
+        raise ValueError("z must be [n, n, c_z]")
+    _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, w_o=w_o), torch.bfloat16, z.device)
+    if mask is not None and (mask.dtype != torch.uint8 or mask.device != z.device or not mask.is_contiguous()):
+        raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    if rows_per_chunk is None:
+        if budget_bytes is None:
+            raise ValueError("give rows_per_chunk or budget_bytes")
+        rows_per_chunk = int(lib.tri_attn_block_chunk_rows(n, cz, h, c, BF16, ctypes.c_size_t(int(budget_bytes))))
+        if rows_per_chunk == 0:
+            raise ValueError("the budget does not hold even one pair row")
+    need = int(lib.tri_attn_block_fwd_chunked_workspace_size(n, cz, h, c, BF16, int(rows_per_chunk)))
+    if need == 0:
+        _check(-1, "tri_attn_block_fwd_chunked_workspace_size")
+    workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+    y = torch.empty_like(z)
+    st = lib.tri_attn_block_fwd_chunked(n, cz, h, c, BF16, int(rows_per_chunk), _ptr(z), _ptr(gamma), _ptr(beta),
+                                        ctypes.c_float(eps), _ptr(w_qkvg), _ptr(w_bias), _ptr(w_o), _ptr(mask), _ptr(y),
+                                        _ptr(workspace), ctypes.c_size_t(need), _stream(z.device))
+    _check(st, "tri_attn_block_fwd_chunked")
+    return y, int(rows_per_chunk), need
 
 
 def __getattr__(name):

@@ -443,4 +443,92 @@ int tri_attn_out_proj_bwd(int n_pairs, int c_in, int c_out, int dtype, const voi
   return hip_status(launch_proj_bwd(a, false, (bf16*)dw, nullptr, nullptr, nullptr, (hipStream_t)stream));
 }
 
+// ---------------------------------------------------------------------------
+// Chunked inference of the starting-node block.  The workspace holds the full
+// pair bias (every query row needs all of it) and, for one chunk of R pair
+// rows, the projections, the attention outputs and statistics, plus the
+// attention forward's own workspace; each region is 256-byte aligned.
+struct ChunkLayout {
+  size_t bias, q, k, v, gate, out, attn, mean, rstd, lse, fws, fws_bytes, total;
+};
+
+static ChunkLayout chunk_layout(int n, int h, int c, int R) {
+  ChunkLayout L{};
+  const size_t per_rows = (size_t)R * n * h * c * 2;  // one bf16 [R][..] projection
+  L.bias = 0;
+  L.q = align256(L.bias + (size_t)h * n * n * 2);
+  L.k = align256(L.q + per_rows);
+  L.v = align256(L.k + per_rows);
+  L.gate = align256(L.v + per_rows);
+  L.out = align256(L.gate + per_rows);
+  L.attn = align256(L.out + per_rows);
+  L.mean = align256(L.attn + per_rows);
+  L.rstd = align256(L.mean + (size_t)R * n * 4);
+  L.lse = align256(L.rstd + (size_t)R * n * 4);
+  L.fws = align256(L.lse + (size_t)R * h * n * 4);
+  L.fws_bytes = align256(fwd_workspace_bytes(n, h));
+  L.total = L.fws + L.fws_bytes;
+  return L;
+}
+
+size_t tri_attn_block_fwd_chunked_workspace_size(int n, int cz, int h, int c, int dtype, int rows_per_chunk) {
+  if (check_proj(n, n, cz, h, c, dtype) != TRI_ATTN_OK) return 0;
+  if (check_common(n, n, h, c, dtype, 0) != TRI_ATTN_OK) return 0;
+  if (rows_per_chunk < 1 || rows_per_chunk > n) return 0;
+  return chunk_layout(n, h, c, rows_per_chunk).total;
+}
+
+int tri_attn_block_chunk_rows(int n, int cz, int h, int c, int dtype, size_t workspace_budget) {
+  if (tri_attn_block_fwd_chunked_workspace_size(n, cz, h, c, dtype, 1) == 0) return 0;
+  int lo = 0, hi = n;  // largest R in [1, n] whose workspace fits, 0 if none
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (chunk_layout(n, h, c, mid).total <= workspace_budget) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_per_chunk, const void* z,
+                               const void* ln_gamma, const void* ln_beta, float ln_eps, const void* w_qkvg,
+                               const void* w_bias, const void* w_o, const uint8_t* mask, void* y, void* workspace,
+                               size_t workspace_bytes, tri_attn_stream_t stream) {
+  int st = check_proj(n, n, cz, h, c, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  if ((st = check_common(n, n, h, c, dtype, 0)) != TRI_ATTN_OK) return st;
+  if (rows_per_chunk < 1 || rows_per_chunk > n) return TRI_ATTN_EINVAL;
+  if (!(ln_eps > 0.0f) || !(ln_eps < 1.0f)) return TRI_ATTN_EINVAL;
+  const void* a16[] = {z, ln_gamma, ln_beta, w_qkvg, w_bias, w_o, y};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  const ChunkLayout L = chunk_layout(n, h, c, rows_per_chunk);
+  if ((st = check_ws(workspace, workspace_bytes, L.total)) != TRI_ATTN_OK) return st;
+  char* ws = (char*)workspace;
+  bf16* bias = (bf16*)(ws + L.bias);
+  void *q = ws + L.q, *k = ws + L.k, *v = ws + L.v, *gate = ws + L.gate, *out = ws + L.out, *attn = ws + L.attn;
+  float *mean = (float*)(ws + L.mean), *rstd = (float*)(ws + L.rstd), *lse = (float*)(ws + L.lse);
+  const bf16* zb = (const bf16*)z;
+  bf16* yb = (bf16*)y;
+  // pass 1: the bias of every pair row (the projections of this pass are overwritten by pass 2)
+  for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
+    const int rr = min(rows_per_chunk, n - r0);
+    st = tri_attn_ln_proj_fwd(rr, n, cz, h, c, dtype, zb + (size_t)r0 * n * cz, ln_gamma, ln_beta, ln_eps, w_qkvg,
+                              w_bias, q, k, v, gate, bias + (size_t)r0 * n, mean, rstd, stream);
+    if (st != TRI_ATTN_OK) return st;
+  }
+  // pass 2: per chunk, projections, attention over the full bias, output linear into y's rows
+  for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
+    const int rr = min(rows_per_chunk, n - r0);
+    st = tri_attn_ln_proj_fwd(rr, n, cz, h, c, dtype, zb + (size_t)r0 * n * cz, ln_gamma, ln_beta, ln_eps, w_qkvg,
+                              w_bias, q, k, v, gate, bias + (size_t)r0 * n, mean, rstd, stream);
+    if (st != TRI_ATTN_OK) return st;
+    st = tri_attn_fwd(rr, n, h, c, dtype, 0, q, k, v, bias, gate, mask ? mask + (size_t)r0 * n : nullptr, out, attn,
+                      lse, ws + L.fws, L.fws_bytes, stream);
+    if (st != TRI_ATTN_OK) return st;
+    st = tri_attn_out_proj_fwd(rr * n, h * c, cz, dtype, out, w_o, yb + (size_t)r0 * n * cz, stream);
+    if (st != TRI_ATTN_OK) return st;
+  }
+  return TRI_ATTN_OK;
+}
+
 }  // extern "C"
