@@ -509,12 +509,21 @@ int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_
   float *mean = (float*)(ws + L.mean), *rstd = (float*)(ws + L.rstd), *lse = (float*)(ws + L.lse);
   const bf16* zb = (const bf16*)z;
   bf16* yb = (bf16*)y;
-  // pass 1: the bias of every pair row (the projections of this pass are overwritten by pass 2)
+  // pass 1: the bias of every pair row, by the front end's bias-only variant (same arithmetic; it writes the
+  // LayerNorm statistics too, into the chunk's statistics area, and no projection)
   for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
     const int rr = min(rows_per_chunk, n - r0);
-    st = tri_attn_ln_proj_fwd(rr, n, cz, h, c, dtype, zb + (size_t)r0 * n * cz, ln_gamma, ln_beta, ln_eps, w_qkvg,
-                              w_bias, q, k, v, gate, bias + (size_t)r0 * n, mean, rstd, stream);
-    if (st != TRI_ATTN_OK) return st;
+    ProjArgs pa{};
+    pa.P = rr * n;
+    pa.n = n;
+    pa.hs = (long long)n * n;
+    pa.eps = ln_eps;
+    pa.x = zb + (size_t)r0 * n * cz;
+    pa.gamma = (const bf16*)ln_gamma; pa.beta = (const bf16*)ln_beta;
+    pa.w = (const bf16*)w_qkvg; pa.wb = (const bf16*)w_bias;
+    pa.bias = bias + (size_t)r0 * n;
+    pa.mean = (float*)mean; pa.rstd = (float*)rstd;
+    if ((st = hip_status(launch_proj_fwd(pa, true, (hipStream_t)stream, true))) != TRI_ATTN_OK) return st;
   }
   // pass 2: per chunk, projections, attention over the full bias, output linear into y's rows
   for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {

@@ -91,7 +91,9 @@ __device__ __forceinline__ bf16x8 weight_chunk(const ProjArgs& a, int row, int c
 }  // namespace
 
 // ---------------------------------------------------------------------------
-template <bool FRONT>
+// BIAS_ONLY (front end): LayerNorm statistics and the pair-bias block only, by
+// the same arithmetic as the full kernel (the chunked inference's first pass).
+template <bool FRONT, bool BIAS_ONLY = false>
 __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int M = FRONT ? FRONT_M : 128;
@@ -171,6 +173,9 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
     const int ia = FRONT ? pc / a.n : 0, ib = FRONT ? pc - ia * a.n : 0;
 #pragma unroll
     for (int oc = 0; oc < M / 32; oc++) {
+      if constexpr (BIAS_ONLY) {
+        if (oc != M / 32 - 1) continue;
+      }
       f32x16 acc = zero16();
 #pragma unroll
       for (int kb = 0; kb < 4; kb++) acc = mma32(lds_c_op(sW + (oc * 32 + l32) * PW_ROW + 32 * kb, g), xo[kb], acc);
@@ -529,10 +534,13 @@ size_t proj_workspace_bytes(int P, bool front) {
   return b;
 }
 
-hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st) {
+hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st, bool bias_only) {
   const int grid = grid_for(a.P);
   hipError_t e;
-  if (front) {
+  if (front && bias_only) {
+    if ((e = set_smem(proj_fwd_kernel<true, true>, fwd_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_fwd_kernel<true, true>), dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
+  } else if (front) {
     if ((e = set_smem(proj_fwd_kernel<true>, fwd_smem(true))) != hipSuccess) return e;
     hipLaunchKernelGGL(proj_fwd_kernel<true>, dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
   } else {
