@@ -228,20 +228,28 @@ __device__ __forceinline__ Op<float> lds_tr_op(const float* tile, int pitch, int
 }
 
 // LDS swizzles of the 32 x 32 bf16 tiles (64-byte rows, no padding): the
-// element (row r, column c) lives at the returned element offset.  Each makes
-// every access pattern of its tiles free of bank conflicts (64 banks x 4 B):
-//  * swz16 (K, Q, dA tiles: 16-byte row reads and writes, transposing reads):
-//    the 16-byte chunk index is XORed with ((r >> 2) ^ (r >> 4)) & 3;
-//  * swz8 (dS^T tiles: 8-byte row writes / reads, transposing reads): the
-//    8-byte chunk index is XORed with a bit permutation of (r >> 2) & 7.
+// element (row r, column c) lives at the returned element offset.  They are
+// chosen against gfx950's LDS banking as its bank-conflict counter shows it:
+//  * 8-byte reads, plain and transposing: 32 consecutive lanes per pass over
+//    64 banks of 4 bytes;
+//  * 16-byte reads: 16 lanes per pass, namely the 4-lane groups of a half-wave
+//    whose group index has even (or odd) bit parity; each 8-byte half of the
+//    access is checked over the 64 banks on its own;
+//  * 8-byte writes: 16 consecutive lanes per pass, 16-byte writes 8, over 32
+//    banks.
+// Every access pattern of these tiles is free of conflicts under that model:
+//  * swz16 (K, Q, dA, V tiles: 16-byte row reads and writes, transposing
+//    reads): the 16-byte chunk index is XORed with (r >> 2) & 3;
+//  * swz8 (dS^T tiles: 8-byte row writes and reads, transposing reads): the
+//    8-byte chunk index is XORed with the bits (r2, r1 ^ r4, r3) of r, lowest
+//    first.
 // Both keep every 4-element (8-byte) group contiguous, and swz16 every
 // 8-element (16-byte) group.
 __device__ __forceinline__ int swz16(int r, int c) {
-  return r * TILE + ((((c >> 3) ^ (r >> 2) ^ (r >> 4)) & 3) << 3) + (c & 7);
+  return r * TILE + ((((c >> 3) ^ (r >> 2)) & 3) << 3) + (c & 7);
 }
 __device__ __forceinline__ int swz8(int r, int c) {
-  const int a = (r >> 2) & 7;
-  const int t = (((a >> 1) & 1) << 2) | ((a & 1) << 1) | (a >> 2);
+  const int t = ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 4)) & 1) << 1) | (((r >> 3) & 1) << 2);
   return r * TILE + ((((c >> 2) ^ t) & 7) << 2) + (c & 3);
 }
 
