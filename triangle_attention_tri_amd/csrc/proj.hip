@@ -34,8 +34,6 @@ constexpr int PJ_WAVES = 8;
 constexpr int PJ_THREADS = 64 * PJ_WAVES;
 constexpr int FRONT_M = 544;     // 512 q/k/v/gate rows + one 32-row block holding the PH bias rows
 constexpr int PW_ROW = 136;      // LDS pitch of row-read weight tiles: 16 B bank shift per row
-constexpr int PW_T_FRONT = 552;  // LDS pitch of the transposed front weights (20-bank shift per row)
-constexpr int PW_T_PLAIN = 136;
 constexpr int PD_FRONT = 544;    // pitch of the staged dT tile: row stride == 64 B mod 256 for
 constexpr int PD_PLAIN = 160;    // conflict-free transposing reads
 constexpr int PX = 160;
@@ -86,6 +84,28 @@ __device__ __forceinline__ bf16x8 weight_chunk(const ProjArgs& a, int row, int c
   if (!FRONT || row < 512) return *reinterpret_cast<const bf16x8*>(a.w + row * CZ + c8);
   if (row - 512 < PH) return *reinterpret_cast<const bf16x8*>(a.wb + (row - 512) * CZ + c8);
   return (bf16x8)(0);
+}
+
+// Row-major weight tile of the dX kernel, unpadded 256-byte rows with the
+// 16-byte chunk index XORed with 4 (o & 3): the staging writes (16 bytes per
+// lane along a row) and the transposing operand reads (4 consecutive rows per
+// 8-lane group) are both free of LDS bank conflicts.
+__device__ __forceinline__ int wsw(int o, int c) { return o * CZ + ((((c >> 3) ^ ((o & 3) << 2)) & 15) << 3) + (c & 7); }
+
+// A operand (MAP_C) of the transposed weights: lane <-> input channel c0 + l32,
+// contraction <-> output rows o0 + 16u + 8g + e, read down the row-major tile.
+__device__ __forceinline__ Op<bf16> w_tr_op(const bf16* sW, int o0, int c0, int lane) {
+  const int G = lane >> 4, jp = lane & 15, g = lane >> 5;
+  const int c = c0 + 16 * (G & 1) + 4 * (jp & 3);
+  const int o = o0 + (jp >> 2);
+  Op<bf16> op;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const bf16x4 lo = lds_read_tr(sW + wsw(o + tr_row<MAP_C>(u, 0, g), c));
+    const bf16x4 hi = lds_read_tr(sW + wsw(o + tr_row<MAP_C>(u, 1, g), c));
+    op.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  return op;
 }
 
 }  // namespace
@@ -231,15 +251,12 @@ template <bool FRONT>
 __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int M = FRONT ? FRONT_M : 128;
-  constexpr int PT = FRONT ? PW_T_FRONT : PW_T_PLAIN;
-  bf16* sWT = reinterpret_cast<bf16*>(smem);  // [128 input channels][PT]: W transposed
-  float* sG = reinterpret_cast<float*>(smem + CZ * PT * 2);
+  bf16* sW = reinterpret_cast<bf16*>(smem);  // [M output rows][128 input channels], wsw layout
+  float* sG = reinterpret_cast<float*>(smem + M * CZ * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, l32 = lane & 31;
   for (int q = tid; q < M * 16; q += PJ_THREADS) {
     const int row = q >> 4, c8 = (q & 15) * 8;
-    const bf16x8 val = weight_chunk<FRONT>(a, row, c8);
-#pragma unroll
-    for (int e = 0; e < 8; e++) sWT[(c8 + e) * PT + row] = val[e];
+    *reinterpret_cast<bf16x8*>(sW + wsw(row, c8)) = weight_chunk<FRONT>(a, row, c8);
   }
   if (FRONT && tid < CZ) sG[tid] = (float)a.gamma[tid];
   __syncthreads();
@@ -261,7 +278,7 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dx_kernel(ProjArgs a) {
       const Op<bf16> bop = bnext;
       if (kb + 1 < M / 32) bnext = gather_dt<FRONT>(a, kb + 1, pc, ia, ib, g);
 #pragma unroll
-      for (int ch = 0; ch < 4; ch++) acc[ch] = mma32(lds_c_op(sWT + (ch * 32 + l32) * PT + 32 * kb, g), bop, acc[ch]);
+      for (int ch = 0; ch < 4; ch++) acc[ch] = mma32(w_tr_op(sW, 32 * kb, ch * 32, lane), bop, acc[ch]);
     }
     // acc[ch][r]: gradient of input channel ch*32 + mrow(g, r) of pair p
     if constexpr (!FRONT) {
@@ -366,16 +383,18 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dw_kernel(ProjArgs a) {
   constexpr int DCH = M / 8 / 16;        // full 16-byte chunks per thread per pair row (16 threads a pair)
   bf16* sD = reinterpret_cast<bf16*>(smem);             // [2][32][PD]
   bf16* sX = sD + 2 * 32 * PD;                          // [2][32][PX]
-  float* sG = reinterpret_cast<float*>(sX + 2 * 32 * PX);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (FRONT && tid < CZ) {
-    sG[tid] = (float)a.gamma[tid];
-    sG[CZ + tid] = (float)a.beta[tid];
-  }
   const int ntile = (a.P + 31) / 32;
   const int per = (ntile + gridDim.x - 1) / gridDim.x;
   const int t0 = blockIdx.x * per, t1 = min(ntile, t0 + per);
   const int pl = tid >> 4, sub = tid & 15;  // staging: 16 threads per pair
+  // the LayerNorm affine parameters of this thread's 8 channels 8 sub .. 8 sub + 7
+  float gam[8], bet[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    gam[e] = FRONT ? (float)a.gamma[8 * sub + e] : 0.0f;
+    bet[e] = FRONT ? (float)a.beta[8 * sub + e] : 0.0f;
+  }
 
   V16 dpre[DCH];
   V16 xpre;
@@ -427,10 +446,7 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dw_kernel(ProjArgs a) {
     bf16x8 xv = __builtin_bit_cast(bf16x8, xpre);
     if constexpr (FRONT) {
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        const int ch = 8 * sub + e;
-        xv[e] = (bf16)ln_apply((float)xv[e], mpre, rpre, sG[ch], sG[CZ + ch]);
-      }
+      for (int e = 0; e < 8; e++) xv[e] = (bf16)ln_apply((float)xv[e], mpre, rpre, gam[e], bet[e]);
     }
     if (!lpre) xv = (bf16x8)(0);
     *reinterpret_cast<bf16x8*>(sX + (buf * 32 + pl) * PX + 8 * sub) = xv;
@@ -440,7 +456,6 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_dw_kernel(ProjArgs a) {
 #pragma unroll
   for (int s = 0; s < BPW; s++) acc[s] = zero16();
   const int ibk = wave & 3;  // every block a wave owns has column block wave % 4
-  __syncthreads();           // gamma / beta visible to stash
   if (t0 < t1) {
     issue(t0);
     stash(0);
@@ -514,9 +529,9 @@ template <typename K> hipError_t set_smem(K kernel, size_t bytes) {
 }
 
 constexpr size_t fwd_smem(bool front) { return (size_t)(front ? FRONT_M : 128) * PW_ROW * 2 + 2 * CZ * 4; }
-constexpr size_t dx_smem(bool front) { return (size_t)CZ * (front ? PW_T_FRONT : PW_T_PLAIN) * 2 + CZ * 4; }
+constexpr size_t dx_smem(bool front) { return (size_t)(front ? FRONT_M : 128) * CZ * 2 + CZ * 4; }
 constexpr size_t dw_smem(bool front) {
-  return (size_t)2 * 32 * (front ? PD_FRONT : PD_PLAIN) * 2 + 2 * 32 * PX * 2 + 2 * CZ * 4;
+  return (size_t)2 * 32 * (front ? PD_FRONT : PD_PLAIN) * 2 + 2 * 32 * PX * 2;
 }
 
 int grid_for(int P) {
