@@ -130,13 +130,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void fwd_kernel(FwdA
   const long long bias_lane = ((long long)(h * nt + min(jt, nt - 1)) * nt * 64 + lane) * 16;
 
   // key masks: one word per (row, key tile); keys past n are never kept.
-  // Without a mask only the key count decides, one word per thread.
-  if (a.mask == nullptr) {
-    for (int idx = tid; idx < R * nt; idx += 256) {
-      const int left = n - (idx % nt) * TILE;
-      sMask[idx / nt][idx % nt] = left >= TILE ? 0xffffffffu : ((1u << left) - 1u);
-    }
-  } else {
+  // Without a mask the tile loop derives the word from the key count.
+  if (a.mask != nullptr) {
     for (int idx = w; idx < R * nt; idx += 4) {
       const int rr = idx / nt, kt = idx % nt;
       const int row = min(row0 + rr, G.n_rows - 1);
@@ -222,7 +217,8 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void fwd_kernel(FwdA
 #pragma unroll
     for (int rr = 0; rr < R; rr++) {
       if (!rvalid[rr]) continue;
-      const uint32_t mbits = sMask[rr][kt];
+      // without a mask only the key count decides (scalar arithmetic, no LDS read)
+      const uint32_t mbits = a.mask != nullptr ? sMask[rr][kt] : (n - k0 >= TILE ? 0xffffffffu : (1u << (n - k0)) - 1u);
       Op<T> kop;
       if constexpr (sizeof(T) == 2)
         kop = swz_c_op(&sKV[buf][rr][0][0], l32, g);
