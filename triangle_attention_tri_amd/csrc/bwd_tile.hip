@@ -613,14 +613,16 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
     q_base[u] = q_which ? a.dA + ((long long)q_rowc * G.H + h) * n * C : a.q + q_rowc * G.qkv_row + headq;
     l_src[u] = (q_which ? a.Dsum : a.lse) + ((long long)q_rowc * G.H + h) * n;
   }
-  const long long q_pos = q_which ? C : G.qkv_pos;
+  // bytes per query position (below 2^32: the host bounds h * n * c * 4), so
+  // each staging address is one 32 x 32 -> 64-bit multiply-add
+  const uint32_t q_pos_bytes = (uint32_t)((q_which ? C : G.qkv_pos) * (long long)sizeof(T));
   V16 qpre[NQ];
   float lpre[NQ];
   auto issue_q = [&](int jt) __attribute__((always_inline)) {
-    const int jj = min(jt * TILE + q_jr, n - 1);
+    const uint32_t jj = (uint32_t)min(jt * TILE + q_jr, n - 1);
 #pragma unroll
     for (int u = 0; u < NQ; u++) {
-      qpre[u] = reinterpret_cast<const V16*>(q_base[u] + jj * q_pos)[q_ch];
+      qpre[u] = reinterpret_cast<const V16*>(reinterpret_cast<const char*>(q_base[u]) + (uint64_t)jj * q_pos_bytes)[q_ch];
       lpre[u] = l_src[u][jj];
     }
   };
