@@ -244,3 +244,16 @@ def test_chunked_block_contract(lib):
     assert call(y=fake_ptr(2)) == EINVAL
     assert call(eps=0.0) == EINVAL
     assert call(ws_bytes=size(8) - 1) == EWORKSPACE
+
+
+def test_chunked_binding_rejects_mask_shape():
+    """The binding checks the mask's shape before any call into the library (a smaller mask would be
+    read past its end)."""
+    import torch
+    n, cz = 8, 128
+    bf = dict(dtype=torch.bfloat16)
+    z = torch.zeros(n, n, cz, **bf)
+    args = (z, torch.ones(cz, **bf), torch.zeros(cz, **bf), torch.zeros(512, cz, **bf), torch.zeros(4, cz, **bf),
+            torch.zeros(cz, 128, **bf))
+    with pytest.raises(ValueError, match="mask must be"):
+        ta.block_fwd_chunked(*args, mask=torch.ones(n, n - 1, dtype=torch.uint8), rows_per_chunk=4)

@@ -333,6 +333,8 @@ def block_fwd_chunked(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_c
     _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, w_o=w_o), torch.bfloat16, z.device)
     if mask is not None and (mask.dtype != torch.uint8 or mask.device != z.device or not mask.is_contiguous()):
         raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    if mask is not None and tuple(mask.shape) != (n, n):
+        raise ValueError(f"mask must be [n, n] = [{n}, {n}], got {tuple(mask.shape)}")
     if rows_per_chunk is None:
         if budget_bytes is None:
             raise ValueError("give rows_per_chunk or budget_bytes")
