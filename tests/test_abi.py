@@ -255,5 +255,35 @@ def test_chunked_binding_rejects_mask_shape():
     z = torch.zeros(n, n, cz, **bf)
     args = (z, torch.ones(cz, **bf), torch.zeros(cz, **bf), torch.zeros(512, cz, **bf), torch.zeros(4, cz, **bf),
             torch.zeros(cz, 128, **bf))
-    with pytest.raises(ValueError, match="mask must be"):
+    with pytest.raises(ValueError, match="mask must have shape"):
         ta.block_fwd_chunked(*args, mask=torch.ones(n, n - 1, dtype=torch.uint8), rows_per_chunk=4)
+
+
+def test_attention_binding_shape_checks():
+    """fwd / bwd reject tensors whose shapes do not match the layouts of the C ABI, before any call into the
+    library (the kernels would read past the end of a smaller tensor)."""
+    import torch
+    n_rows, n, h, c = 3, 8, 4, 32
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.zeros(n_rows, h, n, c, **bf)
+    bias = torch.zeros(h, n, n, **bf)
+    gate = torch.zeros(n_rows, n, h, c, **bf)
+    lse = torch.zeros(n_rows, h, n)
+    with pytest.raises(ValueError, match="gate must have shape"):
+        ta.fwd(q, q, q, bias, torch.zeros(n_rows, n - 1, h, c, **bf))
+    with pytest.raises(ValueError, match="k must have shape"):
+        ta.fwd(q, q[:, :, :-1].contiguous(), q, bias, gate)
+    with pytest.raises(ValueError, match="bias must have shape"):
+        ta.fwd(q, q, q, torch.zeros(h, n, n - 1, **bf), gate)
+    with pytest.raises(ValueError, match="mask must have shape"):
+        ta.fwd(q, q, q, bias, gate, torch.ones(n, n, dtype=torch.uint8))  # n_rows < n: one row per processed row
+    with pytest.raises(ValueError, match="q must have shape"):
+        ta.fwd(q, q, q, bias, gate, ending=True)  # the ending node takes the full [n, h, n, c] tensors
+    with pytest.raises(ValueError, match="lse must have shape"):
+        ta.bwd(q, q, q, bias, gate, None, q, lse[:, :, :-1].contiguous(), gate)
+    with pytest.raises(TypeError, match="lse must be"):
+        ta.bwd(q, q, q, bias, gate, None, q, lse.to(torch.float64), gate)
+    with pytest.raises(TypeError, match="mask must be"):
+        ta.bwd(q, q, q, bias, gate, torch.ones(n_rows, n, dtype=torch.int32), q, lse, gate)
+    with pytest.raises(ValueError, match="attn_residual must have shape"):
+        ta.bwd(q, q, q, bias, gate, None, q, lse, gate, attn_residual=torch.zeros(1, h, n, c, dtype=torch.int8))

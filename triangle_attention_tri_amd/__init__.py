@@ -111,6 +111,31 @@ def _dims(q, bias):
     return n_rows, n, h, c
 
 
+def _expect(name, t, shape):
+    """Shape check before any library call: a smaller tensor would be read past its end."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {list(shape)}, got {list(t.shape)}")
+
+
+def _check_mask(mask, device, n_rows, n):
+    import torch
+    if mask is None:
+        return
+    if mask.dtype != torch.uint8 or mask.device != device or not mask.is_contiguous():
+        raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    _expect("mask", mask, (n_rows, n))
+
+
+def _check_attention_shapes(q, k, v, bias, gate, n_rows, n, h, c, **more):
+    """Layouts of the C ABI (both nodes: the ending node's tensors are the caller's full pair tensors, n_rows = n):
+    q/k/v and attn [n_rows, h, n, c], bias [h, n, n], gate/out/dout [n_rows, n, h, c], lse [n_rows, h, n]."""
+    shapes = dict(q=(n_rows, h, n, c), k=(n_rows, h, n, c), v=(n_rows, h, n, c), bias=(h, n, n),
+                  gate=(n_rows, n, h, c), attn=(n_rows, h, n, c), attn_residual=(n_rows, h, n, c),
+                  lse=(n_rows, h, n), dout=(n_rows, n, h, c))
+    for name, t in dict(q=q, k=k, v=v, bias=bias, gate=gate, **more).items():
+        _expect(name, t, shapes[name])
+
+
 def _prep(tensors, dtype, device):
     for name, t in tensors.items():
         if t is None:
@@ -150,9 +175,8 @@ def fwd(q, k, v, bias, gate, mask=None, ending: bool = False, workspace=None, re
     if ending:
         n_rows = n
     _prep(dict(q=q, k=k, v=v, bias=bias, gate=gate), q.dtype, q.device)
-    if mask is not None:
-        if mask.dtype != torch.uint8 or mask.device != q.device or not mask.is_contiguous():
-            raise TypeError("mask must be a contiguous uint8 tensor on the same device")
+    _check_attention_shapes(q, k, v, bias, gate, n_rows, n, h, c)
+    _check_mask(mask, q.device, n_rows, n)
     need = int(lib.tri_attn_fwd_workspace_size(n_rows, n, h, c, dt))
     if need == 0:
         _check(-2 if c != 32 else -1, "tri_attn_fwd_workspace_size")
@@ -185,6 +209,11 @@ def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, worksp
     if ending:
         n_rows = n
     _prep(dict(q=q, k=k, v=v, bias=bias, gate=gate, attn=attn, dout=dout), q.dtype, q.device)
+    _check_attention_shapes(q, k, v, bias, gate, n_rows, n, h, c, attn=attn, lse=lse, dout=dout,
+                            attn_residual=attn_residual)
+    _check_mask(mask, q.device, n_rows, n)
+    if lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise TypeError("lse must be a contiguous float32 tensor on the same device")
     need = int(lib.tri_attn_bwd_workspace_size(n_rows, n, h, c, dt))
     if need == 0:
         _check(-2 if c != 32 else -1, "tri_attn_bwd_workspace_size")
@@ -331,10 +360,7 @@ def block_fwd_chunked(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_c
     if n != n2:
         raise ValueError("z must be [n, n, c_z]")
     _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, w_o=w_o), torch.bfloat16, z.device)
-    if mask is not None and (mask.dtype != torch.uint8 or mask.device != z.device or not mask.is_contiguous()):
-        raise TypeError("mask must be a contiguous uint8 tensor on the same device")
-    if mask is not None and tuple(mask.shape) != (n, n):
-        raise ValueError(f"mask must be [n, n] = [{n}, {n}], got {tuple(mask.shape)}")
+    _check_mask(mask, z.device, n, n)
     if rows_per_chunk is None:
         if budget_bytes is None:
             raise ValueError("give rows_per_chunk or budget_bytes")
