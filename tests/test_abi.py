@@ -287,3 +287,30 @@ def test_attention_binding_shape_checks():
         ta.bwd(q, q, q, bias, gate, torch.ones(n_rows, n, dtype=torch.int32), q, lse, gate)
     with pytest.raises(ValueError, match="attn_residual must have shape"):
         ta.bwd(q, q, q, bias, gate, None, q, lse, gate, attn_residual=torch.zeros(1, h, n, c, dtype=torch.int8))
+
+
+def test_projection_binding_shape_checks():
+    """The front-end and output-linear bindings check weight, statistics and gradient shapes before any call
+    into the library."""
+    import torch
+    n, cz, h, c = 8, 128, 4, 32
+    bf = dict(dtype=torch.bfloat16)
+    z = torch.zeros(n, n, cz, **bf)
+    g, b = torch.ones(cz, **bf), torch.zeros(cz, **bf)
+    w, wb = torch.zeros(4 * h * c, cz, **bf), torch.zeros(h, cz, **bf)
+    with pytest.raises(ValueError, match="w_qkvg must have shape"):
+        ta.ln_proj_fwd(z, g, b, w[:-1].contiguous(), wb)
+    with pytest.raises(ValueError, match="gamma must have shape"):
+        ta.ln_proj_fwd(z, g[:-1].contiguous(), b, w, wb)
+    dqkv = torch.zeros(n, h, n, c, **bf)
+    dgate = torch.zeros(n, n, h, c, **bf)
+    stat = torch.zeros(n, n)
+    with pytest.raises(ValueError, match="dbias must have shape"):
+        ta.ln_proj_bwd(z, g, b, stat, stat, w, wb, dqkv, dqkv, dqkv, dgate, torch.zeros(h, n, n - 1, **bf))
+    with pytest.raises(TypeError, match="mean must be"):
+        ta.ln_proj_bwd(z, g, b, stat.bfloat16(), stat, w, wb, dqkv, dqkv, dqkv, dgate, torch.zeros(h, n, n, **bf))
+    w_o = torch.zeros(cz, h * c, **bf)
+    with pytest.raises(ValueError, match="o must be"):
+        ta.out_proj_fwd(torch.zeros(n, n, h, c - 1, **bf), w_o)
+    with pytest.raises(ValueError, match="dy must have shape"):
+        ta.out_proj_bwd(torch.zeros(n, n, h, c, **bf), w_o, torch.zeros(n, n - 1, cz, **bf))

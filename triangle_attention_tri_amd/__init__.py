@@ -241,6 +241,20 @@ def bwd(q, k, v, bias, gate, mask, attn, lse, dout, ending: bool = False, worksp
 # ---------------------------------------------------------------------------
 # LayerNorm + projection front end and output linear (bf16, c_z = h*c = 128)
 
+def _check_front_shapes(cz, h, c, gamma, beta, w_qkvg, w_bias):
+    _expect("gamma", gamma, (cz,))
+    _expect("beta", beta, (cz,))
+    _expect("w_qkvg", w_qkvg, (4 * h * c, cz))
+    _expect("w_bias", w_bias, (h, cz))
+
+
+def _check_out_shapes(o, w_o, dy=None):
+    c_out, c_in = w_o.shape
+    if o.dim() < 3 or o.shape[-2] * o.shape[-1] != c_in:
+        raise ValueError(f"o must be [..., h, c] with h * c = {c_in}, got {list(o.shape)}")
+    _expect("dy", dy, tuple(o.shape[:-2]) + (c_out,))
+
+
 def ln_proj_fwd(z, gamma, beta, w_qkvg, w_bias, h: int = 4, c: int = 32, eps: float = 1e-5):
     """z [R,N,cz] -> (q, k, v [R,h,N,c], gate [R,N,h,c], bias [h,R,N], mean, rstd [R,N] fp32).
 
@@ -251,6 +265,7 @@ def ln_proj_fwd(z, gamma, beta, w_qkvg, w_bias, h: int = 4, c: int = 32, eps: fl
     lib = load()
     n_rows, n, cz = z.shape
     _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias), torch.bfloat16, z.device)
+    _check_front_shapes(cz, h, c, gamma, beta, w_qkvg, w_bias)
     dev = z.device
     q = torch.empty((n_rows, h, n, c), dtype=z.dtype, device=dev)
     k, v = torch.empty_like(q), torch.empty_like(q)
@@ -275,6 +290,17 @@ def ln_proj_bwd(z, gamma, beta, mean, rstd, w_qkvg, w_bias, dq, dk, dv, dgate, d
     n_rows, n, cz = z.shape
     _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, dq=dq, dk=dk, dv=dv, dgate=dgate,
                dbias=dbias), torch.bfloat16, z.device)
+    _check_front_shapes(cz, h, c, gamma, beta, w_qkvg, w_bias)
+    if n_rows != n:
+        raise ValueError("row slices: call the C ABI with the full dbias tensor at a row offset")
+    for name, t in dict(dq=dq, dk=dk, dv=dv).items():
+        _expect(name, t, (n_rows, h, n, c))
+    _expect("dgate", dgate, (n_rows, n, h, c))
+    _expect("dbias", dbias, (h, n, n))
+    for name, t in dict(mean=mean, rstd=rstd).items():
+        if t.dtype != torch.float32 or t.device != z.device or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous float32 tensor on the same device")
+        _expect(name, t, (n_rows, n))
     need = int(lib.tri_attn_ln_proj_bwd_workspace_size(n_rows, n, cz, h, c, BF16))
     if need == 0:
         _check(-2, "tri_attn_ln_proj_bwd_workspace_size")
@@ -298,6 +324,7 @@ def out_proj_fwd(o, w_o):
     c_out, c_in = w_o.shape
     n_pairs = o.numel() // c_in
     _prep(dict(o=o, w_o=w_o), torch.bfloat16, o.device)
+    _check_out_shapes(o, w_o)
     y = torch.empty(o.shape[:-2] + (c_out,), dtype=o.dtype, device=o.device)
     st = lib.tri_attn_out_proj_fwd(n_pairs, c_in, c_out, BF16, _ptr(o), _ptr(w_o), _ptr(y), _stream(o.device))
     _check(st, "tri_attn_out_proj_fwd")
@@ -311,6 +338,7 @@ def out_proj_bwd(o, w_o, dy, workspace=None):
     c_out, c_in = w_o.shape
     n_pairs = o.numel() // c_in
     _prep(dict(o=o, w_o=w_o, dy=dy), torch.bfloat16, o.device)
+    _check_out_shapes(o, w_o, dy)
     need = int(lib.tri_attn_out_proj_bwd_workspace_size(n_pairs, c_in, c_out, BF16))
     if need == 0:
         _check(-2, "tri_attn_out_proj_bwd_workspace_size")
