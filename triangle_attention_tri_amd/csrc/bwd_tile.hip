@@ -732,7 +732,12 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
   // (16x16x32 MFMAs); (b) the pair-bias slab = sum of the group's NR dS tiles
   // (rounded operands, added in row order), this wave storing part rg of each
   // of its tiles
+  // Phase 2 runs at raised wave priority: its chain of LDS reads, small MFMAs
+  // and stores is short and latency-bound, and the SIMD's other wave (in
+  // phase 1) fills the issue slots it leaves.  Measured: main kernel about 4%
+  // faster than with equal priorities; a fixed priority per wave group was not.
   auto phase2 = [&](int jt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
     const int b = jt & 1;
     f32x4 acc[QBW];
 #pragma unroll
@@ -788,6 +793,7 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
       else
         *reinterpret_cast<V8*>(dst) = (V8){sum[0], sum[1]};
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   issue_q(0);
