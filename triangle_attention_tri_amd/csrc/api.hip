@@ -163,6 +163,17 @@ int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const vo
   a.out = (T*)out; a.attn = (T*)attn; a.lse = lse;
   a.bias_prep = (float*)ws;
   a.attn_res = attn_res;
+  if constexpr (sizeof(T) == 2) {
+    // Few rows (a row slice, a small chunk): when the two-row grid would not
+    // fill the device once (3 workgroups per CU), one row per workgroup doubles
+    // the workgroups.  Each row's arithmetic is the same in both forms.
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+      const long long blocks2 = (long long)((geo.n + 127) / 128) * ((geo.n_rows + 1) / 2) * geo.H;
+      if (blocks2 < 3ll * cus) return hip_status(launch_fwd<T, 1>(a, st));
+    }
+  }
   return hip_status(launch_fwd<T, FWD_R>(a, st));
 }
 

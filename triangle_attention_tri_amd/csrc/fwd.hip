@@ -102,7 +102,7 @@ hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStr
 constexpr int FWD_MAX_TILES = 64;
 
 template <typename T, int R>
-__global__ __launch_bounds__(256, (sizeof(T) == 2 ? 3 : 2)) void fwd_kernel(FwdArgs<T> a) {
+__global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void fwd_kernel(FwdArgs<T> a) {
   constexpr int KP = TILE + kpad<T>();            // LDS row pitch (elements)
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte vector
   constexpr int CHUNKS = C / EPV;                 // vectors per 32-element row
@@ -362,6 +362,7 @@ hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
 }
 
 template hipError_t launch_fwd<bf16, 2>(const FwdArgs<bf16>&, hipStream_t);
+template hipError_t launch_fwd<bf16, 1>(const FwdArgs<bf16>&, hipStream_t);
 template hipError_t launch_fwd<float, 2>(const FwdArgs<float>&, hipStream_t);
 
 }  // namespace tri
