@@ -192,7 +192,9 @@ def test_row_slice_key_ranges(device):
     """bf16 with several key ranges and a row count that is not a multiple of the row group:
     n = 200 splits the keys into two ranges of four tiles, and 37 rows leave the last group of
     four with one live row (padded rows, padded dQ partials).  Each row's outputs match the full
-    run bit for bit; the slice's dbias matches the oracle."""
+    run bit for bit; the slice's dbias matches the oracle.  On a 256-CU device the 37-row slice
+    launches the one-row forward form (its two-row grid would not fill the device) and the full
+    call the two-row form, so this also checks that the two forms agree bit for bit."""
     n, h = 200, 4
     log(f"row slice with key ranges n={n}")
     xc = inputs.attn_inputs(n, h, 32, torch.bfloat16, seed=12)
