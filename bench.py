@@ -9,8 +9,11 @@ recomputed QK^T, dP, dV, dK, dQ backward).
 Prints ONE JSON line.  Durations are measured with HIP events recorded on the
 stream the kernels run on.  Each recorded event leaves a few microseconds of
 idle time between the kernels it separates, so the timed steps carry only the
-events the roofline needs (around the main backward kernel); the per-stage
-split comes from a second pass.
+events the roofline needs (around one launch of the main backward kernel per
+step); the per-stage split comes from a second pass.  The smaller
+configurations (N=64 fp32, N=256, N=384 with key padding, N=640 with a wide
+bias at both nodes: the crops the pages train at) are timed the same way and
+reported under "configs"; ``--config i`` times only configuration i.
 """
 from __future__ import annotations
 
@@ -241,18 +244,188 @@ def time_chunked(lib, hip, dev, stream, n, steps, warmup, rows_list=(768, 128, 3
     return res
 
 
+class AttnCase:
+    """One attention workload resident on the GPU: seeded inputs, outputs, workspaces and the C ABI calls of a
+    step (tri_attn_fwd + tri_attn_bwd, or the residual-compensated pair)."""
+
+    def __init__(self, lib, hip, dev, stream, n, dtype, seed, bias_std=1.0, valid_len=None, H=4, c=32):
+        import torch
+
+        import triangle_attention_tri_amd as ta
+        from triangle_attention_tri_amd import inputs
+        self.lib, self.hip, self.stream, self.n, self.H, self.c = lib, hip, stream, n, H, c
+        self.dt = ta.BF16 if dtype == torch.bfloat16 else ta.F32
+        self.xc = inputs.attn_inputs(n, H, c, dtype, seed=seed, bias_std=bias_std, valid_len=valid_len)
+        x = self.x = {k: (None if v is None else v.to(dev)) for k, v in self.xc.items()}
+        self.valid = n if valid_len is None else valid_len
+        self.out = torch.empty_like(x["gate"])
+        self.attn = torch.empty_like(x["q"])
+        self.lse = torch.empty((n, H, n), dtype=torch.float32, device=dev)
+        self.grads = [torch.empty_like(x[k]) for k in ("q", "k", "v", "bias", "gate")]
+        self.ws_bytes = ta.workspace_size(n, n, H, c, dtype)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.fws_bytes = ta.fwd_workspace_size(n, n, H, c, dtype)
+        self.fws = torch.empty(self.fws_bytes, dtype=torch.uint8, device=dev)
+        self.chunk = ta.bwd_chunk_rows(n, n, H, c, dtype)
+        self.chunks = -(-n // self.chunk)
+        self.res = torch.empty((n, H, n, c), dtype=torch.int8, device=dev) if self.dt == ta.BF16 else None
+        self.events = (ctypes.c_void_p * (4 * self.chunks))()
+        lib.tri_attn_bwd_profiled.argtypes = list(lib.tri_attn_bwd.argtypes) + [ctypes.c_void_p]
+        lib.tri_attn_bwd_profiled.restype = ctypes.c_int
+
+    def step(self, ending: int, fwd_ev=None, bwd_ev=None, rc: bool = False):
+        """fwd_ev: (before, after) the forward or None; bwd_ev: 4 events per backward chunk (None entries skipped)
+        or None for the plain entry point."""
+        P = lambda t: None if t is None else ctypes.c_void_p(t.data_ptr())  # noqa: E731
+        x, n, H, c, lib, st = self.x, self.n, self.H, self.c, self.lib, self.stream
+        sz = ctypes.c_size_t
+        if fwd_ev is not None and fwd_ev[0] is not None:
+            self.hip.record(fwd_ev[0], st)
+        if rc:
+            r = lib.tri_attn_fwd_rc(n, n, H, c, self.dt, ending, P(x["q"]), P(x["k"]), P(x["v"]), P(x["bias"]),
+                                    P(x["gate"]), P(x["mask"]), P(self.out), P(self.attn), P(self.res), P(self.lse),
+                                    P(self.fws), sz(self.fws_bytes), st)
+        else:
+            r = lib.tri_attn_fwd(n, n, H, c, self.dt, ending, P(x["q"]), P(x["k"]), P(x["v"]), P(x["bias"]),
+                                 P(x["gate"]), P(x["mask"]), P(self.out), P(self.attn), P(self.lse), P(self.fws),
+                                 sz(self.fws_bytes), st)
+        assert r == 0, r
+        if fwd_ev is not None and fwd_ev[1] is not None:
+            self.hip.record(fwd_ev[1], st)
+        g = [P(t) for t in self.grads]
+        if rc:
+            r = lib.tri_attn_bwd_rc(n, n, H, c, self.dt, ending, P(x["q"]), P(x["k"]), P(x["v"]), P(x["bias"]),
+                                    P(x["gate"]), P(x["mask"]), P(self.attn), P(self.res), P(self.lse),
+                                    P(x["dout"]), *g, P(self.ws), sz(self.ws_bytes), st)
+            assert r == 0, r
+            return
+        common = (n, n, H, c, self.dt, ending, P(x["q"]), P(x["k"]), P(x["v"]), P(x["bias"]), P(x["gate"]),
+                  P(x["mask"]), P(self.attn), P(self.lse), P(x["dout"]), *g, P(self.ws), sz(self.ws_bytes), st)
+        if bwd_ev is None:
+            r = lib.tri_attn_bwd(*common)
+        else:
+            for i in range(4 * self.chunks):
+                self.events[i] = bwd_ev[i]
+            r = lib.tri_attn_bwd_profiled(*common, ctypes.cast(self.events, ctypes.c_void_p))
+        assert r == 0, r
+
+    def timed(self, ending: int, steps: int, warmup: int, stages: bool = True):
+        """K timed steps carrying only two events each, around one launch of the main backward kernel (its
+        launch time, for the roofline; the chunks take turns), then (stages=True) K steps with events between
+        every stage.  Each recorded event leaves a few microseconds of idle time between the kernels it
+        separates, which is why the timed steps carry no others."""
+        import torch
+        hip, ch = self.hip, self.chunks
+        for _ in range(warmup):
+            self.step(ending)
+        torch.cuda.synchronize()
+        # one chunk's launch per step carries the two events (chunks in rotation), so every step has the same
+        # two idle gaps whatever the chunk count
+        main_ev = [(hip.event(), hip.event()) for _ in range(steps)]
+        bwd_ev = []
+        for s_ in range(steps):
+            evs = [None] * (4 * ch)
+            m = s_ % ch
+            evs[4 * m + 1], evs[4 * m + 2] = main_ev[s_]
+            bwd_ev.append(evs)
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, self.stream)
+        for s_ in range(steps):
+            self.step(ending, bwd_ev=bwd_ev[s_])
+        hip.record(t1, self.stream)
+        torch.cuda.synchronize()
+        total = hip.ms(t0, t1) / steps
+        launches = [hip.ms(a, b) for (a, b) in main_ev]
+        out = {"ms": total, "main_launch_ms": sum(launches) / len(launches), "main_launches_per_step": ch}
+        if stages:
+            st = {"fwd": 0.0, "bwd_pre": 0.0, "bwd_main": 0.0, "bwd_reduce": 0.0}
+            for _ in range(steps):
+                fe = (hip.event(), hip.event())
+                be = [hip.event() for _ in range(4 * ch)]
+                self.step(ending, fwd_ev=fe, bwd_ev=be)
+                torch.cuda.synchronize()
+                st["fwd"] += hip.ms(fe[0], fe[1])
+                for m in range(ch):
+                    st["bwd_pre"] += hip.ms(be[4 * m], be[4 * m + 1])
+                    st["bwd_main"] += hip.ms(be[4 * m + 1], be[4 * m + 2])
+                    st["bwd_reduce"] += hip.ms(be[4 * m + 2], be[4 * m + 3])
+            out["stages"] = {k: v / steps for k, v in st.items()}
+        return out
+
+    def flops(self):
+        """fwd + bwd: 4 + 10 flops per logit and channel over the valid keys (one recompute of P)."""
+        return 14.0 * self.n * self.n * self.valid * self.H * self.c
+
+    def main_flops_per_launch(self):
+        return 10.0 * self.chunk * self.n * self.valid * self.H * self.c
+
+
+def main_kernel_name(case):
+    return "bwd_group_kernel" if case.dt == 1 else ("bwd_tile_kernel" if case.n <= 256 else "bwd_main_kernel")
+
+
+def config_line(case, res, workload, peak, node):
+    """Per-configuration record: the step, the forward and backward stages and the main backward kernel against
+    its roofline (its own algorithmic flops per launch over its event-timed launch duration)."""
+    ms = res["ms"]
+    tf = case.flops() / (ms * 1e-3) / 1e12
+    ach = case.main_flops_per_launch() / (res["main_launch_ms"] * 1e-3) / 1e12
+    return {"workload": workload, "n": case.n, "node": node, "dtype": "bf16" if case.dt == 1 else "f32",
+            "valid_keys": case.valid, "flops_per_step": case.flops(), "ms_per_step": round(ms, 4),
+            "tflops": round(tf, 2), "peak_tflops": peak, "frac_of_peak": round(tf / peak, 4),
+            "stages_ms": {k: round(v, 4) for k, v in res.get("stages", {}).items()},
+            "main_kernel": {"kernel": main_kernel_name(case), "launch_ms": round(res["main_launch_ms"], 4),
+                            "launches_per_step": res["main_launches_per_step"], "rows_per_launch": case.chunk,
+                            "achieved_tflops": round(ach, 2), "frac": round(ach / peak, 4)}}
+
+
+# The configurations of this workload (seeded as in the tests); index 4 is the headline.
+CONFIGS = {
+    0: dict(n=64, dtype="f32", seed=0, workload="tri_attn_start_fwd_bwd_N64_H4_c32_f32", nodes=(0,)),
+    1: dict(n=256, dtype="bf16", seed=1, workload="tri_attn_start_fwd_bwd_N256_H4_c32_bf16", nodes=(0,)),
+    2: dict(n=384, dtype="bf16", seed=2, valid_len=345,
+            workload="tri_attn_start_fwd_bwd_N384_H4_c32_bf16_keymask345", nodes=(0,)),
+    3: dict(n=640, dtype="bf16", seed=3, bias_std=2.0, workload="tri_attn_fwd_bwd_N640_H4_c32_bf16_bias_std2",
+            nodes=(0, 1)),
+}
+PEAK_FP32_TFLOPS = 157.3
+
+
+def time_configs(lib, hip, dev, stream, which, steps, warmup):
+    import torch
+    lines = []
+    for idx in which:
+        cfg = CONFIGS[idx]
+        dtype = torch.bfloat16 if cfg["dtype"] == "bf16" else torch.float32
+        case = AttnCase(lib, hip, dev, stream, cfg["n"], dtype, cfg["seed"], cfg.get("bias_std", 1.0),
+                        cfg.get("valid_len"))
+        peak = PEAK_BF16_TFLOPS if cfg["dtype"] == "bf16" else PEAK_FP32_TFLOPS
+        for node in cfg["nodes"]:
+            res = case.timed(node, steps, warmup)
+            line = config_line(case, res, cfg["workload"], peak, "end" if node else "start")
+            line["config"] = idx
+            lines.append(line)
+        del case
+        torch.cuda.empty_cache()
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--n", type=int, default=768)
+    ap.add_argument("--config", type=int, default=None, choices=sorted(CONFIGS),
+                    help="time only this smaller configuration and print its record (for profiling runs)")
     ap.add_argument("--cpu-rows", type=int, default=512, help="rows of the oracle CPU sample (0 = skip)")
     ap.add_argument("--no-end", action="store_true", help="skip the ending-node timing")
     ap.add_argument("--no-rc", action="store_true", help="skip the timing of the residual-compensated pair")
     ap.add_argument("--no-chunked", action="store_true", help="skip the chunked block inference timing")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the LayerNorm + projection + attention + output-linear block timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the smaller configurations")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -265,90 +438,12 @@ def main():
     import torch
 
     import triangle_attention_tri_amd as ta
-    from triangle_attention_tri_amd import inputs
 
     lib = ta.load()
     hip = Hip()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    n, H, c = args.n, 4, 32
-    xc = inputs.attn_inputs(n, H, c, torch.bfloat16, seed=4)
-    xd = {k: (None if v is None else v.to(dev)) for k, v in xc.items()}
-    out = torch.empty_like(xd["gate"])
-    attn = torch.empty((n, H, n, c), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((n, H, n), dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty_like(xd[k]) for k in ("q", "k", "v"))
-    dbias, dgate = torch.empty_like(xd["bias"]), torch.empty_like(xd["gate"])
-    ws_bytes = ta.workspace_size(n, n, H, c, torch.bfloat16)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    fws_bytes = ta.fwd_workspace_size(n, n, H, c, torch.bfloat16)
-    fws = torch.empty(fws_bytes, dtype=torch.uint8, device=dev)
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    attn_res = torch.empty((n, H, n, c), dtype=torch.int8, device=dev)
-    bwd_events = (ctypes.c_void_p * 4)()
-    lib.tri_attn_bwd_profiled.argtypes = list(lib.tri_attn_bwd.argtypes) + [ctypes.c_void_p]
-    lib.tri_attn_bwd_profiled.restype = ctypes.c_int
-
-    def step(ending: int, ev=None, rc: bool = False):
-        if ev is not None and ev[0] is not None:
-            hip.record(ev[0], stream)
-        if rc:  # residual-compensated pair (tri_attn_fwd_rc / tri_attn_bwd_rc)
-            st = lib.tri_attn_fwd_rc(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
-                                     P(xd["gate"]), None, P(out), P(attn), P(attn_res), P(lse), P(fws),
-                                     ctypes.c_size_t(fws_bytes), stream)
-            assert st == 0, st
-            st = lib.tri_attn_bwd_rc(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
-                                     P(xd["gate"]), None, P(attn), P(attn_res), P(lse), P(xd["dout"]), P(dq), P(dk),
-                                     P(dv), P(dbias), P(dgate), P(ws), ctypes.c_size_t(ws_bytes), stream)
-            assert st == 0, st
-            return
-        st = lib.tri_attn_fwd(n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]),
-                              P(xd["gate"]), None, P(out), P(attn), P(lse), P(fws), ctypes.c_size_t(fws_bytes), stream)
-        assert st == 0, st
-        common = (n, n, H, c, ta.BF16, ending, P(xd["q"]), P(xd["k"]), P(xd["v"]), P(xd["bias"]), P(xd["gate"]),
-                  None, P(attn), P(lse), P(xd["dout"]), P(dq), P(dk), P(dv), P(dbias), P(dgate), P(ws),
-                  ctypes.c_size_t(ws_bytes), stream)
-        if ev is None:
-            st = lib.tri_attn_bwd(*common)
-        else:
-            for i in range(4):
-                bwd_events[i] = ev[1 + i]  # None: not recorded
-            st = lib.tri_attn_bwd_profiled(*common, ctypes.cast(bwd_events, ctypes.c_void_p))
-        assert st == 0, st
-
-    def timed(ending: int, steps: int, warmup: int):
-        """K timed steps, then K more with events between every stage.
-
-        Each recorded event leaves a few microseconds of idle time between the
-        kernels it separates, so the timed steps record only the two events
-        around the main backward kernel (its launch time, for the roofline).
-        The per-stage split comes from the second, separately timed pass.
-        """
-        for _ in range(warmup):
-            step(ending)
-        torch.cuda.synchronize()
-        main_ev = [(hip.event(), hip.event()) for _ in range(steps)]
-        t0, t1 = hip.event(), hip.event()
-        torch.cuda.synchronize()
-        hip.record(t0, stream)
-        for s in range(steps):
-            step(ending, (None, None, main_ev[s][0], main_ev[s][1], None))
-        hip.record(t1, stream)
-        torch.cuda.synchronize()
-        total = hip.ms(t0, t1)
-        main_ms = sum(hip.ms(a, b) for a, b in main_ev) / steps
-        evs = [[hip.event() for _ in range(5)] for _ in range(steps)]
-        for s in range(steps):
-            step(ending, evs[s])
-        torch.cuda.synchronize()
-        stages = {"fwd": 0.0, "bwd_pre": 0.0, "bwd_main": 0.0, "dbias_reduce": 0.0}
-        for e in evs:
-            stages["fwd"] += hip.ms(e[0], e[1])
-            stages["bwd_pre"] += hip.ms(e[1], e[2])
-            stages["bwd_main"] += hip.ms(e[2], e[3])
-            stages["dbias_reduce"] += hip.ms(e[3], e[4])
-        return total / steps, {k: v / steps for k, v in stages.items()}, main_ms
 
     if args.copy_calibration_mib > 0:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale the HBM byte counts
@@ -359,39 +454,54 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    ms_step, stages, main_ms = timed(0, args.steps, args.warmup)
-    flops = 14.0 * n ** 3 * H * c
+    if args.config is not None:
+        for line in time_configs(lib, hip, dev, stream, [args.config], args.steps, args.warmup):
+            print(json.dumps(line), flush=True)
+        return
+
+    n, H, c = args.n, 4, 32
+    case = AttnCase(lib, hip, dev, stream, n, torch.bfloat16, seed=4)
+    res = case.timed(0, args.steps, args.warmup)
+    ms_step = res["ms"]
+    flops = case.flops()
     value = flops / (ms_step * 1e-3) / 1e12
 
-    # roofline of the kernel that takes the most time: the main backward kernel (twice the forward's time at
-    # this size), its launch time measured by the events around it in the timed steps
-    work = 10.0 * n ** 3 * H * c
-    achieved = work / (main_ms * 1e-3) / 1e12
+    # roofline of the kernel that takes the most time, the main backward kernel (twice the forward's time at
+    # this size): the algorithmic flops of one launch (10 per logit and channel over the launch's row chunk)
+    # over its average launch duration, from the events around each launch in the timed steps
+    work = case.main_flops_per_launch()
+    achieved = work / (res["main_launch_ms"] * 1e-3) / 1e12
     kernel = "bwd_group_kernel"
     roofline = {"kernel": kernel, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": stored_traffic(kernel), "launch_ms": round(main_ms, 4)}
+                "traffic": stored_traffic(kernel), "launch_ms": round(res["main_launch_ms"], 4),
+                "launches_per_step": res["main_launches_per_step"], "rows_per_launch": case.chunk}
 
     end_ms = None
     if not args.no_end:
-        end_ms = timed(1, max(3, args.steps // 2), 2)[0]
+        end_ms = case.timed(1, max(3, args.steps // 2), 2, stages=False)["ms"]
 
     rc_ms = None
     if not args.no_rc:
         rc_steps = max(3, args.steps // 2)
         for _ in range(2):
-            step(0, rc=True)
+            case.step(0, rc=True)
         t0, t1 = hip.event(), hip.event()
         torch.cuda.synchronize()
         hip.record(t0, stream)
         for _ in range(rc_steps):
-            step(0, rc=True)
+            case.step(0, rc=True)
         hip.record(t1, stream)
         torch.cuda.synchronize()
         rc_ms = hip.ms(t0, t1) / rc_steps
+    xc = case.xc
+    del case
+    torch.cuda.empty_cache()
 
     block = None if args.no_block else time_block(lib, hip, dev, stream, n, max(3, args.steps // 2), 2, args.no_end)
     chunked = None if args.no_chunked else time_chunked(lib, hip, dev, stream, n, 3, 1)
+    configs = None if args.no_configs else time_configs(lib, hip, dev, stream, sorted(CONFIGS),
+                                                        max(5, args.steps // 2), 3)
 
     cpu = None
     if rank == 0 and args.cpu_rows > 0:
@@ -404,10 +514,11 @@ def main():
         "config": {"workload": f"tri_attn_start_fwd_bwd_N{n}_H{H}_c{c}_bf16", "n": n, "h": H, "c": c,
                    "node": "start", "mask": None, "flops_per_step": flops},
         "pct_of_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stages_ms": {k: round(v, 4) for k, v in res["stages"].items()},
         "end_node_ms_per_step": None if end_ms is None else round(end_ms, 4),
         "residual_compensated_ms_per_step": None if rc_ms is None else round(rc_ms, 4),
         "roofline": roofline,
+        "configs": configs,
         "block": block,
         "chunked_block_fwd": chunked,
         "cpu_baseline": cpu,

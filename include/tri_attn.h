@@ -83,7 +83,9 @@ int tri_attn_version(void);
 /* Static text for a status code; never NULL. */
 const char *tri_attn_status_string(int status);
 
-/* Largest n the compiled kernels accept for a dtype (0 for a bad dtype). */
+/* Largest n the compiled kernels accept for a dtype (0 for a bad dtype):
+ * 2048 for bf16 (the forward's per-workgroup table of kept-key words), 736 for
+ * fp32 (the fp32 backward past 256 keys keeps a row's K and V in LDS). */
 int tri_attn_max_n(int dtype);
 
 /* Bytes of device workspace tri_attn_fwd needs for these sizes (0 on bad args). */
@@ -112,8 +114,23 @@ int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending,
                  void *out, void *attn_saved, float *lse,
                  void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
 
-/* Bytes of device workspace tri_attn_bwd needs for these sizes (0 on bad args). */
+/* Bytes of device workspace tri_attn_bwd needs for these sizes (0 on bad args).
+ * The backward processes the call's rows in consecutive chunks of
+ * tri_attn_bwd_chunk_rows rows that reuse one workspace (the gradient reaching
+ * the pre-gate attention, the softmax row terms, and the partial sums of the
+ * chunk's pair-bias and query gradients), so the workspace is bounded by the
+ * chunk, not by n_rows: about 0.48 GB at n = n_rows = 768, h = 4, bf16. */
 size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype);
+
+/* Rows per chunk of the backward for these sizes (0 on bad args); the call
+ * runs ceil(n_rows / chunk) chunks.  The chunking does not change any result:
+ * the pair-bias gradient is summed over rows in the same order as in one pass.
+ * The library picks the chunk from a budget of about 300 MiB of partial sums;
+ * the environment variable TRI_ATTN_BWD_CHUNK_ROWS (a positive integer, read on
+ * every call of this function, tri_attn_bwd_workspace_size and the backward
+ * entry points) replaces that choice, rounded down to whole 32-row blocks and
+ * at least 32 rows; set it before sizing the workspace. */
+int tri_attn_bwd_chunk_rows(int n_rows, int n, int h, int c, int dtype);
 
 /*
  * Backward pass.  Inputs as for the forward plus attn_saved and lse from it and
@@ -136,13 +153,17 @@ int tri_attn_bwd(int n_rows, int n, int h, int c, int dtype, int ending,
 
 /*
  * tri_attn_bwd with per-stage timing: identical arguments and results, plus
- * stage_events, an array of 4 caller-created HIP events recorded on `stream`
- * before the preprocessing kernels (gate gradient, D, bias tiles), before the
- * main backward kernel, before the pair-bias reduction and after it.  A NULL
- * entry is not recorded (each record puts a few microseconds of idle time
- * between the kernels it separates); the array itself must be non-NULL
- * (TRI_ATTN_EINVAL otherwise).  Intended for benchmarks that need the main
- * kernel's own duration.
+ * stage_events, an array of 4 caller-created HIP events per row chunk
+ * (4 * ceil(n_rows / tri_attn_bwd_chunk_rows(...)) entries), recorded on
+ * `stream`: for chunk m, entries 4m .. 4m+3 before its preprocessing, before
+ * its main backward kernel, before its reductions (pair bias, query gradient)
+ * and after them.  The preprocessing (gate gradient, D, the prepared bias
+ * tiles) covers every row of the call in one pass before the first chunk, so
+ * for later chunks entries 4m and 4m+1 mark the same point; only the fp32 path
+ * past 256 keys preprocesses each chunk on its own.  A NULL entry is not recorded (each record puts a few
+ * microseconds of idle time between the kernels it separates); the array
+ * itself must be non-NULL (TRI_ATTN_EINVAL otherwise).  Intended for
+ * benchmarks that need the main kernel's own duration.
  */
 int tri_attn_bwd_profiled(int n_rows, int n, int h, int c, int dtype, int ending,
                           const void *q, const void *k, const void *v, const void *bias,

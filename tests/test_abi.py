@@ -128,6 +128,28 @@ def test_workspace_sizes(lib):
             assert b >= n * 4 * n * 32 * (2 if dt == ta.BF16 else 4) + n * 4 * n * 4
 
 
+def test_backward_chunks(lib):
+    """The backward runs its rows in chunks that bound the workspace: one chunk for small calls, whole 32-row
+    blocks otherwise, and at N=768, H=4 (bf16) a workspace under 0.6 GB (a single pass would need 1.9 GB)."""
+    lib.tri_attn_bwd_chunk_rows.argtypes = [ctypes.c_int] * 5
+    assert lib.tri_attn_bwd_chunk_rows(8, 8, 2, 16, ta.BF16) == 0
+    assert lib.tri_attn_bwd_chunk_rows(0, 8, 2, 32, ta.BF16) == 0
+    for dt in (ta.BF16, ta.F32):
+        for n in (1, 17, 64, 256):
+            assert lib.tri_attn_bwd_chunk_rows(n, n, 4, 32, dt) == n
+    for n, dt in ((640, ta.BF16), (768, ta.BF16), (960, ta.BF16), (2048, ta.BF16), (300, ta.F32), (736, ta.F32)):
+        ch = lib.tri_attn_bwd_chunk_rows(n, n, 4, 32, dt)
+        assert 32 <= ch <= n and (ch == n or ch % 32 == 0), (n, dt, ch)
+        # a row slice never gets a larger chunk than the full call
+        assert lib.tri_attn_bwd_chunk_rows(n // 2, n, 4, 32, dt) == min(ch, n // 2)
+    assert lib.tri_attn_bwd_chunk_rows(768, 768, 4, 32, ta.BF16) < 768
+    assert lib.tri_attn_bwd_workspace_size(768, 768, 4, 32, ta.BF16) <= 600_000_000
+    # beyond the input-sized dA and D of every row: one chunk of at least 32 rows of partial sums, the prepared
+    # bias tiles and the running pair-bias sum
+    n = 2048
+    assert lib.tri_attn_bwd_workspace_size(n, n, 4, 32, ta.BF16) <= n * 4 * n * (32 * 2 + 4) + 700_000_000
+
+
 def test_binding_rejects_bad_inputs():
     q = torch.zeros((4, 2, 4, 32), dtype=torch.float16)
     with pytest.raises(TypeError):

@@ -163,3 +163,49 @@ def test_block_fwd_chunked(device):
     y, r, need = ta.block_fwd_chunked(*w, mask=xd["mask"], budget_bytes=sizes[37] + 100)
     torch.cuda.synchronize()
     assert r >= 37 and need <= sizes[37] + 100 and torch.equal(y, y_full)
+
+
+def test_out_proj_n768(device):
+    """Output linear forward and backward at the block's full size (768 x 768 = 589,824 pairs): the persistent
+    multi-tile loop, the cross-tile prefetch and the per-workgroup weight-gradient partials all run here."""
+    n = 768
+    log(f"out_proj n={n} ({n * n} pairs)")
+    g = torch.Generator().manual_seed(768)
+    o = torch.randn((n, n, H, C), generator=g).bfloat16()
+    w_o = (torch.randn((CZ, H * C), generator=g) / 128 ** 0.5).bfloat16()
+    dy = torch.randn((n, n, CZ), generator=g).bfloat16()
+    od, wd, dyd = o.to(device), w_o.to(device), dy.to(device)
+    y = ta.out_proj_fwd(od, wd)
+    d_o, dw_o = ta.out_proj_bwd(od, wd, dyd)
+    torch.cuda.synchronize()
+    errs = {"y": assert_close("y", y.cpu(), B.out_proj_fwd(o, w_o), TOL)}
+    ref = B.out_proj_bwd(o, w_o, dy)
+    errs["do"] = assert_close("do", d_o.cpu(), ref["do"], TOL)
+    errs["dw_o"] = assert_close("dw_o", dw_o.cpu(), ref["dw_o"], TOL)
+    log(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("ending", [False, True])
+def test_block_n768(device, ending):
+    """The whole block at its full size (z [768, 768, 128] bf16, H=4, c=32, c_z=128): front end -> attention
+    (starting or ending node) -> output linear, forward and backward, in the launch configuration the benchmark
+    times.  Every element of y, dz, dgamma, dbeta, dw_qkvg, dw_bias and dw_o is compared with the fp64 block
+    oracle (the oracle runs the full attention forward and backward over all 768 rows)."""
+    n = 768
+    log(f"block n={n} ending={ending}: GPU")
+    x = inputs.block_inputs(n, seed=4, affine=True)
+    xd = dev(x, device)
+    y, saved = ta.block_fwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"], ending=ending)
+    grads = ta.block_bwd(xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"], saved, xd["dy"],
+                         ending=ending)
+    torch.cuda.synchronize()
+    got = {"y": y.cpu(), **{k: v.cpu() for k, v in grads.items()}}
+    del saved, grads, y, xd
+    torch.cuda.empty_cache()
+    log(f"block n={n} ending={ending}: oracle")
+    ref = B.block_bwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], x["w_o"], x["dy"], H, C, ending=ending)
+    errs = {}
+    for name in ("y", "dz", "dgamma", "dbeta", "dw_qkvg", "dw_bias", "dw_o"):
+        errs[name] = assert_close(name, got[name], ref[name], TOL)
+    log(" ".join(f"{k}={v:.2e}" for k, v in errs.items()))

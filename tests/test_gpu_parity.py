@@ -15,7 +15,7 @@ import torch
 import oracle
 import triangle_attention_tri_amd as ta
 from triangle_attention_tri_amd import inputs
-from tests.helpers import assert_close, np64
+from tests.helpers import assert_close, assert_lse, lse_tol, np64
 
 pytestmark = pytest.mark.gpu
 
@@ -95,7 +95,10 @@ def check_full(name, xc, res, tol, ending=False):
     got = gpu_rows(res, rows, ending)
     errs = {}
     for key in OUT_KEYS + GRAD_KEYS:
-        errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
+        if key == "lse":
+            errs[key] = assert_lse(f"{name}:lse", got[key], ref[key], lse_tol(tol))
+        else:
+            errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
     log(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     return errs
 
@@ -105,7 +108,10 @@ def check_sampled(name, xc, res, tol, ending, rows, qsel):
     got = gpu_rows(res, rows, ending)
     errs = {}
     for key in OUT_KEYS + ("dq", "dk", "dv", "dgate"):
-        errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
+        if key == "lse":
+            errs[key] = assert_lse(f"{name}:lse", got[key], ref[key], lse_tol(tol))
+        else:
+            errs[key] = assert_close(f"{name}:{key}", got[key], ref[key], tol)
     db_ref = oracle_dbias_queries(xc, qsel, ending)
     errs["dbias"] = assert_close(f"{name}:dbias", got["dbias"][:, qsel], db_ref, tol)
     log(name, " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
@@ -351,3 +357,47 @@ def test_profiled_stage_events(device):
     assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
     log(f"main backward kernel at n={n}: {ms.value:.3f} ms")
     assert ms.value > 0.0
+
+
+@pytest.mark.parametrize("case", ["bf16_n768_start", "bf16_n256_end_mask", "fp32_n300_rows"])
+def test_backward_chunking_bitwise(device, case, monkeypatch):
+    """The backward runs its rows in chunks (tri_attn_bwd_chunk_rows) that carry the pair-bias gradient as an fp32
+    running sum in a single pass's order.  Every output is bit for bit that of one pass over all rows (and of
+    32-row chunks), for the bf16 row-group kernel at both nodes and for the fp32 rows kernel."""
+    n, dtype, ending, mask = {"bf16_n768_start": (768, torch.bfloat16, False, None),
+                              "bf16_n256_end_mask": (256, torch.bfloat16, True, "random"),
+                              "fp32_n300_rows": (300, torch.float32, False, "random")}[case]
+    xc = inputs.attn_inputs(n, 4, 32, dtype, seed=77, bias_std=1.5)
+    if mask:
+        xc["mask"] = inputs.random_mask(n, seed=78, p_keep=0.8, full_rows=(3,))
+    xd = to_dev(xc, device)
+    monkeypatch.delenv("TRI_ATTN_BWD_CHUNK_ROWS", raising=False)
+    default_chunk = ta.bwd_chunk_rows(n, n, 4, 32, dtype)
+    base = run_gpu(xd, ending)
+    for forced in (n, 32):
+        monkeypatch.setenv("TRI_ATTN_BWD_CHUNK_ROWS", str(forced))
+        assert ta.bwd_chunk_rows(n, n, 4, 32, dtype) == forced
+        res = run_gpu(xd, ending)
+        for key in base:
+            assert torch.equal(res[key], base[key]), f"{case}: {key} differs with {forced}-row chunks " \
+                                                     f"(default {default_chunk})"
+    log(f"{case}: default chunk {default_chunk}, one pass and 32-row chunks bitwise equal")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("node", ["start", "end"])
+def test_largest_bf16_size(device, node):
+    """bf16 at the largest accepted n (2048: the forward's table of kept-key words per workgroup holds 64 key
+    tiles), H=2, with a key mask that drops a whole row: sixteen key ranges, 32-row backward chunks, sampled rows
+    and exact dbias columns against the oracle, at both nodes."""
+    n, h = ta.max_n(torch.bfloat16), 2
+    assert n == 2048
+    log(f"largest bf16 size n={n} h={h} node={node}")
+    xc = inputs.attn_inputs(n, h, 32, torch.bfloat16, seed=2048, bias_std=1.5)
+    xc["mask"] = inputs.random_mask(n, seed=2049, p_keep=0.9, full_rows=(5,))
+    ending = node == "end"
+    res = run_gpu(to_dev(xc, device), ending)
+    rng = np.random.default_rng(2048)
+    rows = sorted({0, 5, n // 2, n - 1, *rng.choice(n, 2, replace=False).tolist()})
+    qsel = sorted({0, 31, n - 1, *rng.choice(n, 2, replace=False).tolist()})
+    check_sampled(f"n{n}:{node}", xc, res, 2e-2, ending, rows, qsel)

@@ -21,7 +21,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_size", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path",
+__all__ = ["fwd", "bwd", "workspace_size", "bwd_chunk_rows", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path",
            "load", "ln_proj_fwd", "ln_proj_bwd", "out_proj_fwd", "out_proj_bwd", "block_fwd", "block_bwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -53,6 +53,8 @@ def load():
     lib.tri_attn_fwd.restype = i
     lib.tri_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.tri_attn_bwd_workspace_size.restype = sz
+    lib.tri_attn_bwd_chunk_rows.argtypes = [i, i, i, i, i]
+    lib.tri_attn_bwd_chunk_rows.restype = i
     lib.tri_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
     lib.tri_attn_bwd.restype = i
     lib.tri_attn_fwd_rc.argtypes = [i, i, i, i, i, i] + [vp] * 11 + [sz, vp]
@@ -157,6 +159,12 @@ def workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:
     """Backward workspace bytes."""
     import torch
     return int(load().tri_attn_bwd_workspace_size(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
+
+
+def bwd_chunk_rows(n_rows: int, n: int, h: int, c: int, dtype) -> int:
+    """Rows per chunk of the backward (it runs its rows in chunks that reuse one workspace)."""
+    import torch
+    return int(load().tri_attn_bwd_chunk_rows(n_rows, n, h, c, BF16 if dtype == torch.bfloat16 else F32))
 
 
 def fwd_workspace_size(n_rows: int, n: int, h: int, c: int, dtype) -> int:

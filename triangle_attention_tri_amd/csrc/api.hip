@@ -4,14 +4,18 @@
 #include "../../include/tri_attn.h"
 #include "proj.hpp"
 
+#include <algorithm>
+#include <cstdlib>
+
 namespace tri {
 template <typename T, int R> hipError_t launch_fwd(const FwdArgs<T>&, hipStream_t);
 size_t fwd_workspace_bytes(int n, int h);
 template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T, int R> size_t bwd_main_smem(int n);
-template <typename T, int KPW> hipError_t launch_bwd_tile(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
+template <typename T> hipError_t launch_bwd_prep(const BwdArgs<T>&, hipStream_t);
+template <typename T, int KPW> hipError_t launch_bwd_tile_chunk(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T> size_t tile_smem(int kpw);
-template <int KPW> hipError_t launch_bwd_group(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template <int KPW> hipError_t launch_bwd_group_chunk(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
 size_t group_smem(int kpw);
 }  // namespace tri
 
@@ -24,32 +28,28 @@ constexpr int FWD_R = 2;
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Rows per backward workgroup: the largest compiled count whose LDS fits.
-// bf16 compiles 1, 2, 4 and fp32 1, 2 (larger counts spill registers).
-template <typename T> int pick_bwd_rows(int n);
-template <> int pick_bwd_rows<bf16>(int n) {
-  if (bwd_main_smem<bf16, 4>(n) <= LDS_LIMIT) return 4;
-  if (bwd_main_smem<bf16, 2>(n) <= LDS_LIMIT) return 2;
-  if (bwd_main_smem<bf16, 1>(n) <= LDS_LIMIT) return 1;
-  return 0;
-}
-template <> int pick_bwd_rows<float>(int n) {
+// Longest key axis of the forward: its per-workgroup table of kept-key words
+// holds 64 key tiles.  bf16 runs use the row-group backward kernel, whose LDS
+// does not depend on n, so this is the bf16 limit.
+constexpr int FWD_MAX_N = 64 * 32;
+
+// fp32 runs past the tile kernel's 256 keys use the rows kernel (bwd.hip),
+// which keeps R rows' K and V for the whole key axis in LDS: rows per
+// workgroup is the largest compiled count (1 or 2) whose LDS fits.
+int pick_rows_f32(int n) {
   if (bwd_main_smem<float, 2>(n) <= LDS_LIMIT) return 2;
   if (bwd_main_smem<float, 1>(n) <= LDS_LIMIT) return 1;
   return 0;
 }
 
-int pick_rows(int dtype, int n) {
-  return dtype == TRI_ATTN_BF16 ? pick_bwd_rows<bf16>(n) : pick_bwd_rows<float>(n);
-}
-
 int max_n(int dtype) {
-  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return 0;
-  int lo = 1, hi = 1 << 16;
-  if (pick_rows(dtype, lo) == 0) return 0;
+  if (dtype == TRI_ATTN_BF16) return FWD_MAX_N;
+  if (dtype != TRI_ATTN_F32) return 0;
+  int lo = 1, hi = FWD_MAX_N;
+  if (pick_rows_f32(lo) == 0) return 0;
   while (lo < hi) {  // largest n with a fitting row count
     int mid = lo + (hi - lo + 1) / 2;
-    if (pick_rows(dtype, mid) > 0) lo = mid;
+    if (pick_rows_f32(mid) > 0) lo = mid;
     else hi = mid - 1;
   }
   return lo;
@@ -111,45 +111,100 @@ int pick_kpw(int dtype, int n) {
   return smem <= LDS_LIMIT ? kpw : 0;
 }
 
+// Row chunks of the backward.  The pair-bias partials of a chunk's row groups
+// and the dQ partials of its key ranges grow with the rows processed at once
+// (as rows x n^2), so a call is run as consecutive row slices of at most
+// `chunk` rows that reuse one workspace;
+// the pair-bias gradient is carried between them as an fp32 running sum.  A
+// chunk keeps at most BWD_CHUNK_BUDGET bytes of these intermediates, rounded
+// down to whole 32-row blocks (so that a chunk's grid is a whole number of
+// device-filling waves at the benchmarked sizes), and holds at least 32 rows.
+// Chunks start at multiples of 32 rows, so they split no row group, and the
+// summation order of every reduction is that of a single pass: results do not
+// depend on the chunking.
+constexpr size_t BWD_CHUNK_BUDGET = (size_t)300 << 20;
+
 struct WsLayout {
-  size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, trash, total;
-  int rows, groups, kpw, nsplit, slab_rows;
+  size_t dA, Dsum, slabs, bias_prep, tslab, dq_part, trash, dbias_acc, total;
+  int rows, groups, kpw, nsplit, slab_rows, chunk;
 };
+
+// intermediate bytes per row of a chunk: the pair-bias and dQ partials (the
+// tiled kernels, whose preprocessing covers every row of the call at once), or
+// dA, D and the pair-bias partials (the rows kernel, preprocessed per chunk)
+size_t bwd_row_bytes(int n, int h, int dtype, int kpw, int rows_per_group) {
+  const size_t es = dtype == TRI_ATTN_BF16 ? 2 : 4;
+  const size_t nt = (size_t)(n + TILE - 1) / TILE;
+  size_t b = kpw > 0 ? 0 : (size_t)h * n * C * es + (size_t)h * n * sizeof(float);
+  if (kpw > 0) {
+    const int slab_div = dtype == TRI_ATTN_BF16 ? BF16_GROUP_ROWS : 1;
+    b += (size_t)h * nt * nt * 1024 * es / slab_div;
+    const int ns = pick_nsplit(dtype, n);
+    if (ns > 1) b += (size_t)ns * h * dq_part_queries(n) * C * es;
+  } else {
+    b += (size_t)h * n * n * sizeof(float) / rows_per_group;
+  }
+  return b;
+}
+
+// TRI_ATTN_BWD_CHUNK_ROWS (environment, read on every call): rows per chunk in
+// place of the budget's choice, rounded down to whole 32-row blocks (at least
+// one); unset, empty or not a positive number: the budget decides.
+long long chunk_rows_override() {
+  const char* s = std::getenv("TRI_ATTN_BWD_CHUNK_ROWS");
+  if (s == nullptr || *s == 0) return 0;
+  char* end = nullptr;
+  const long long v = std::strtoll(s, &end, 10);
+  return (end != s && *end == 0 && v > 0) ? v : 0;
+}
+
+int bwd_chunk_rows(int n_rows, int n, int h, int dtype, int kpw, int rows_per_group) {
+  const size_t per_row = bwd_row_bytes(n, h, dtype, kpw, rows_per_group);
+  const long long forced = chunk_rows_override();
+  long long r = forced > 0 ? forced : (long long)(BWD_CHUNK_BUDGET / per_row);
+  if (r >= n_rows) return n_rows;
+  // whole 32-row blocks (a multiple of every row-group size), at least one
+  r = std::max<long long>(32, r & ~31ll);
+  return (int)std::min<long long>(r, n_rows);
+}
 
 WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
   WsLayout L{};
   const size_t es = dtype == TRI_ATTN_BF16 ? 2 : 4;
   const size_t nt = (size_t)(n + TILE - 1) / TILE;
   L.kpw = pick_kpw(dtype, n);
+  L.rows = L.kpw > 0 ? 1 : (dtype == TRI_ATTN_F32 ? pick_rows_f32(n) : 0);
+  if (L.kpw == 0 && L.rows == 0) return L;
+  const int cr = L.chunk = bwd_chunk_rows(n_rows, n, h, dtype, L.kpw, L.rows);
+  const size_t pre_rows = L.kpw > 0 ? n_rows : cr;  // rows whose dA and D are held at once
   L.dA = 0;
-  L.Dsum = align256(L.dA + (size_t)n_rows * h * n * C * es);
-  const size_t after_d = align256(L.Dsum + (size_t)n_rows * h * n * sizeof(float));
+  L.Dsum = align256(L.dA + pre_rows * h * n * C * es);
+  const size_t after_d = align256(L.Dsum + pre_rows * h * n * sizeof(float));
+  size_t acc_elems;  // fp32 running sum of the pair-bias gradient between chunks, in the reduction's order
+  size_t end;
   if (L.kpw > 0) {
-    L.rows = 1;
     L.nsplit = pick_nsplit(dtype, n);
     L.bias_prep = after_d;
     // prepared bias: bf16 operand tiles for bf16 runs, fp32 for fp32 runs (plus one zero tile)
     L.tslab = align256(L.bias_prep + ((size_t)h * nt * nt + 1) * 1024 * (dtype == TRI_ATTN_BF16 ? 2 : 4));
     // bf16 sums the dS tiles of each row group before storing them
-    L.slab_rows = dtype == TRI_ATTN_BF16 ? (n_rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS : n_rows;
+    L.slab_rows = dtype == TRI_ATTN_BF16 ? (cr + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS : cr;
     L.dq_part = align256(L.tslab + (size_t)L.slab_rows * h * nt * nt * 1024 * es);
-    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * dq_part_rows(n_rows) * h *
+    L.trash = align256(L.dq_part + (L.nsplit > 1 ? (size_t)L.nsplit * dq_part_rows(cr) * h *
                                                         dq_part_queries(n) * C * es : 0));
-    L.total = align256(L.trash + BWD_TRASH_BYTES);
-    return L;
+    end = align256(L.trash + BWD_TRASH_BYTES);
+    acc_elems = (size_t)h * nt * nt * 1024;
+  } else {
+    L.groups = (cr + L.rows - 1) / L.rows;
+    L.slabs = after_d;
+    end = align256(L.slabs + (size_t)L.groups * h * n * n * sizeof(float));
+    acc_elems = (size_t)h * n * n;
   }
-  L.rows = pick_rows(dtype, n);
-  if (L.rows == 0) return L;
-  L.groups = (n_rows + L.rows - 1) / L.rows;
-  L.slabs = after_d;
-  L.total = align256(L.slabs + (size_t)L.groups * h * n * n * sizeof(float));
+  L.dbias_acc = end;
+  L.total = cr < n_rows ? align256(end + acc_elems * sizeof(float)) : end;
   return L;
 }
 
-template <typename T, int R> hipError_t launch_bwd_rows(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
-  if constexpr (sizeof(T) == 4 && R > 2) return hipErrorInvalidValue;
-  else return launch_bwd<T, R>(a, st, ev);
-}
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_EHIP; }
 
@@ -177,52 +232,83 @@ int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const vo
   return hip_status(launch_fwd<T, FWD_R>(a, st));
 }
 
+// Arguments of rows c0 .. c0 + rows - 1 of the call: a row slice, with the
+// pointers of the caller's tensors advanced by c0 along the processed-row axis
+// of each layout.  dA and D (the tiled kernels' preprocessing covers every row
+// of the call) advance too; the rows kernel preprocesses each chunk into the
+// start of its buffers.
 template <typename T>
-int do_bwd(const Geo& geo, const WsLayout& L, const void* q, const void* k, const void* v, const void* bias,
-           const void* gate, const uint8_t* mask, const void* attn, const int8_t* attn_res, const float* lse,
-           const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate, void* ws, hipStream_t st,
-           hipEvent_t* ev) {
-  BwdArgs<T> a;
-  a.geo = geo;
-  a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v; a.bias = (const T*)bias;
-  a.gate = (const T*)gate; a.attn = (const T*)attn; a.dout = (const T*)dout;
-  a.mask = mask; a.lse = lse;
-  a.dq = (T*)dq; a.dk = (T*)dk; a.dv = (T*)dv; a.dbias = (T*)dbias; a.dgate = (T*)dgate;
+BwdArgs<T> chunk_args(const Geo& full, int ending, const WsLayout& L, int c0, int rows, const void* q, const void* k,
+                      const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn,
+                      const int8_t* attn_res, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                      void* dbias, void* dgate, void* ws) {
+  const long long kro = (long long)c0 * full.H * full.n * C;  // kernel-order [row][H][n][C] tensors
+  BwdArgs<T> a{};
+  a.geo = make_geo(rows, full.n, full.H, ending);
+  a.q = (const T*)q + c0 * full.qkv_row; a.k = (const T*)k + c0 * full.qkv_row; a.v = (const T*)v + c0 * full.qkv_row;
+  a.bias = (const T*)bias;
+  a.gate = (const T*)gate + c0 * full.pair_row; a.attn = (const T*)attn + kro; a.dout = (const T*)dout + c0 * full.pair_row;
+  a.mask = mask ? mask + c0 * full.mask_row : nullptr;
+  a.lse = lse + (long long)c0 * full.H * full.n;
+  a.dq = (T*)dq + c0 * full.qkv_row; a.dk = (T*)dk + c0 * full.qkv_row; a.dv = (T*)dv + c0 * full.qkv_row;
+  a.dbias = (T*)dbias; a.dgate = (T*)dgate + c0 * full.pair_row;
   char* base = (char*)ws;
-  a.dA = (T*)(base + L.dA);
-  a.Dsum = (float*)(base + L.Dsum);
+  const long long pre0 = L.kpw > 0 ? c0 : 0;
+  a.dA = (T*)(base + L.dA) + pre0 * full.H * full.n * C;
+  a.Dsum = (float*)(base + L.Dsum) + pre0 * full.H * full.n;
   a.slabs = (float*)(base + L.slabs);
-  a.groups = L.groups;
+  a.groups = L.kpw > 0 ? 0 : (rows + L.rows - 1) / L.rows;
   a.bias_prep = (float*)(base + L.bias_prep);
   a.tslab = (T*)(base + L.tslab);
   a.dq_part = base + L.dq_part;
   a.trash = (float*)(base + L.trash);
   a.nsplit = L.nsplit;
-  a.attn_res = attn_res;
+  a.attn_res = attn_res ? attn_res + kro : nullptr;
+  a.dbias_acc = (float*)(base + L.dbias_acc);
+  a.acc_first = c0 == 0;
+  a.acc_last = c0 + rows == full.n_rows;
+  a.slab_rows = sizeof(T) == 2 ? (rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS : rows;
+  a.slab_e = sizeof(T) == 2 ? 16 / BF16_GROUP_ROWS : 8;
+  return a;
+}
+
+// stage_events (optional): 4 events per chunk, see tri_attn_bwd_profiled
+template <typename T>
+int do_bwd(const Geo& geo, int ending, const WsLayout& L, const void* q, const void* k, const void* v,
+           const void* bias, const void* gate, const uint8_t* mask, const void* attn, const int8_t* attn_res,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dbias, void* dgate, void* ws,
+           hipStream_t st, hipEvent_t* ev) {
   if (attn_res != nullptr && L.kpw == 0) return TRI_ATTN_EUNSUPPORTED;  // only the tiled kernels' preprocess reads it
+  auto args = [&](int c0, int rows) {
+    return chunk_args<T>(geo, ending, L, c0, rows, q, k, v, bias, gate, mask, attn, attn_res, lse, dout, dq, dk, dv,
+                         dbias, dgate, ws);
+  };
   hipError_t e;
   if (L.kpw > 0) {
-    a.slab_rows = L.slab_rows;
-    a.slab_e = sizeof(T) == 2 ? 16 / BF16_GROUP_ROWS : 8;
-    if constexpr (sizeof(T) == 2) {
-      // bf16: BF16_GROUP_ROWS rows per workgroup (group-summed dS slabs)
-      switch (L.kpw) {
-        case 1: e = launch_bwd_group<1>(a, st, ev); break;
-        case 2: e = launch_bwd_group<2>(a, st, ev); break;
-        default: return TRI_ATTN_EUNSUPPORTED;
+    // the tiled kernels: one preprocessing pass over every row, then per chunk the main kernel and reductions
+    if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return hip_status(e);
+    if ((e = launch_bwd_prep<T>(args(0, geo.n_rows), st)) != hipSuccess) return hip_status(e);
+  }
+  for (int c0 = 0, ci = 0; c0 < geo.n_rows; c0 += L.chunk, ci++) {
+    const BwdArgs<T> a = args(c0, std::min(L.chunk, geo.n_rows - c0));
+    hipEvent_t* cev = ev ? ev + 4 * ci : nullptr;
+    if (L.kpw > 0) {
+      if (ci > 0 && cev && cev[0] && (e = hipEventRecord(cev[0], st)) != hipSuccess) return hip_status(e);
+      if constexpr (sizeof(T) == 2) {
+        // bf16: BF16_GROUP_ROWS rows per workgroup (group-summed dS slabs)
+        e = L.kpw == 1 ? launch_bwd_group_chunk<1>(a, st, cev) : launch_bwd_group_chunk<2>(a, st, cev);
+      } else {
+        e = L.kpw == 1 ? launch_bwd_tile_chunk<T, 1>(a, st, cev) : launch_bwd_tile_chunk<T, 2>(a, st, cev);
       }
+    } else if constexpr (sizeof(T) == 4) {
+      // fp32 past the tile kernel: the rows kernel, preprocessed per chunk
+      e = L.rows == 2 ? launch_bwd<T, 2>(a, st, cev) : launch_bwd<T, 1>(a, st, cev);
     } else {
-      switch (L.kpw) {
-        case 1: e = launch_bwd_tile<T, 1>(a, st, ev); break;
-        case 2: e = launch_bwd_tile<T, 2>(a, st, ev); break;
-        default: return TRI_ATTN_EUNSUPPORTED;
-      }
+      return TRI_ATTN_EUNSUPPORTED;
     }
-  } else if (L.rows == 4 && sizeof(T) == 2) e = launch_bwd_rows<T, 4>(a, st, ev);
-  else if (L.rows == 2) e = launch_bwd_rows<T, 2>(a, st, ev);
-  else if (L.rows == 1) e = launch_bwd_rows<T, 1>(a, st, ev);
-  else return TRI_ATTN_EUNSUPPORTED;
-  return hip_status(e);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return TRI_ATTN_OK;
 }
 
 }  // namespace
@@ -287,6 +373,11 @@ size_t tri_attn_bwd_workspace_size(int n_rows, int n, int h, int c, int dtype) {
   return ws_layout(n_rows, n, h, dtype).total;
 }
 
+int tri_attn_bwd_chunk_rows(int n_rows, int n, int h, int c, int dtype) {
+  if (check_common(n_rows, n, h, c, dtype, 0) != TRI_ATTN_OK) return 0;
+  return ws_layout(n_rows, n, h, dtype).chunk;
+}
+
 static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
                     const void* v, const void* bias, const void* gate, const uint8_t* mask, const void* attn_saved,
                     const int8_t* attn_res, const float* lse, const void* dout, void* dq, void* dk, void* dv,
@@ -299,13 +390,14 @@ static int bwd_impl(int n_rows, int n, int h, int c, int dtype, int ending, cons
     if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
   const WsLayout L = ws_layout(n_rows, n, h, dtype);
   if (L.rows == 0 && L.kpw == 0) return TRI_ATTN_EUNSUPPORTED;
+  if (attn_res != nullptr && L.kpw == 0) return TRI_ATTN_EUNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < L.total) return TRI_ATTN_EWORKSPACE;
   if (((uintptr_t)workspace & 255u) != 0) return TRI_ATTN_EINVAL;
   const Geo geo = make_geo(n_rows, n, h, ending);
   if (dtype == TRI_ATTN_BF16)
-    return do_bwd<bf16>(geo, L, q, k, v, bias, gate, mask, attn_saved, attn_res, lse, dout, dq, dk, dv, dbias,
+    return do_bwd<bf16>(geo, ending, L, q, k, v, bias, gate, mask, attn_saved, attn_res, lse, dout, dq, dk, dv, dbias,
                         dgate, workspace, s, ev);
-  return do_bwd<float>(geo, L, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk, dv, dbias, dgate,
+  return do_bwd<float>(geo, ending, L, q, k, v, bias, gate, mask, attn_saved, nullptr, lse, dout, dq, dk, dv, dbias, dgate,
                        workspace, s, ev);
 }
 

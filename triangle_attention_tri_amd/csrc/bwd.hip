@@ -278,8 +278,12 @@ __global__ __launch_bounds__(256) void dbias_reduce_kernel(BwdArgs<T> a) {
   const long long total = (long long)G.H * nn;
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= total) return;
-  float s = 0.0f;
+  float s = a.acc_first ? 0.0f : a.dbias_acc[e];  // running sum of the earlier row chunks
   for (int gi = 0; gi < a.groups; gi++) s += a.slabs[(long long)gi * total + e];
+  if (!a.acc_last) {
+    a.dbias_acc[e] = s;
+    return;
+  }
   const int h = (int)(e / nn);
   const int jq = (int)((e / G.n) % G.n);
   const int kk = (int)(e % G.n);
@@ -303,13 +307,9 @@ hipError_t launch_bwd(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
   if (e != hipSuccess) return e;
   if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
   const size_t smem = BwdSmem<T, R>::total(G.n);
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)bwd_main_kernel<T, R>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (per device, no process-wide state)
+  e = hipFuncSetAttribute((const void*)bwd_main_kernel<T, R>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_main_kernel<T, R>), dim3(a.groups, G.H), dim3(256), smem, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -325,9 +325,6 @@ hipError_t launch_bwd(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
 #define TRI_INST(T, R)                                                   \
   template hipError_t launch_bwd<T, R>(const BwdArgs<T>&, hipStream_t, hipEvent_t*); \
   template size_t bwd_main_smem<T, R>(int);
-TRI_INST(bf16, 1)
-TRI_INST(bf16, 2)
-TRI_INST(bf16, 4)
 TRI_INST(float, 1)
 TRI_INST(float, 2)
 #undef TRI_INST

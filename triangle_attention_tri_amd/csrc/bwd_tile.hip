@@ -860,10 +860,9 @@ __global__ __launch_bounds__(512, 1) void bwd_group_kernel(BwdArgs<bf16> a) {
 // dQ = (partial of key range 0 + partial of key range 1 + ...) / sqrt(c), ranges
 // in order.  Eight channels per thread (16-byte loads of bf16 partials).
 template <typename T>
-__global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
+__device__ __forceinline__ void dq_sum(const BwdArgs<T>& a, long long t) {
   constexpr int CPT = 8;
   const Geo& G = a.geo;
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t * CPT >= (long long)G.n_rows * G.H * G.n * C) return;
   const long long e = t * CPT;
   const int c0 = (int)(e % C);
@@ -903,8 +902,10 @@ __global__ __launch_bounds__(256) void dq_sum_kernel(BwdArgs<T> a) {
   }
 }
 
-// dbias[h][j][k] = sum over slabs (rows or row pairs, ascending) of the dS
-// tiles, fp32, rounded once.  One thread per (h, jt, kt, lane, half of the
+// dbias[h][j][k] = sum over slabs (rows or row groups, ascending) of the dS
+// tiles, fp32, rounded once.  With several row chunks the fp32 sum runs on from
+// the previous chunk's running sum (same order, so the result does not depend
+// on the chunking) and only the last chunk rounds and writes dbias.  One thread per (h, jt, kt, lane, half of the
 // lane's 16 registers): 16-byte loads (bf16), eight slabs in flight.
 template <typename T>
 __device__ __forceinline__ void load_half_tile(const T* p, float (&v)[8]);
@@ -920,11 +921,10 @@ template <> __device__ __forceinline__ void load_half_tile<float>(const float* p
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
+__device__ __forceinline__ void dbias_tile_reduce(const BwdArgs<T>& a, long long t) {
   const Geo& G = a.geo;
   const int n = G.n, nt = (n + TILE - 1) / TILE;
   const long long per_row = (long long)G.H * nt * nt * 1024;  // elements per slab
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (t >= per_row / 8) return;
   // first element: [h][jt][kt][part][lane][E] with E = a.slab_e values per
   // lane and part (E = 8: one lane's half; E = 4: two lanes' quarters)
@@ -933,6 +933,11 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   const long long tile = e0 >> 10;
   const int kt = (int)(tile % nt), jt = (int)((tile / nt) % nt), h = (int)(tile / ((long long)nt * nt));
   float s[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  if (!a.acc_first) {  // continue the running sum of the earlier row chunks
+    const f32x4 x = *reinterpret_cast<const f32x4*>(a.dbias_acc + e0), y = *reinterpret_cast<const f32x4*>(a.dbias_acc + e0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) { s[i] = x[i]; s[4 + i] = y[i]; }
+  }
   const T* src = a.tslab + e0;
   int row = 0;
   for (; row + 8 <= a.slab_rows; row += 8) {
@@ -950,6 +955,11 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
 #pragma unroll
     for (int i = 0; i < 8; i++) s[i] += v[i];
   }
+  if (!a.acc_last) {
+    *reinterpret_cast<f32x4*>(a.dbias_acc + e0) = (f32x4){s[0], s[1], s[2], s[3]};
+    *reinterpret_cast<f32x4*>(a.dbias_acc + e0 + 4) = (f32x4){s[4], s[5], s[6], s[7]};
+    return;
+  }
   const int E = a.slab_e;
 #pragma unroll
   for (int i = 0; i < 8; i++) {
@@ -959,92 +969,101 @@ __global__ __launch_bounds__(256) void dbias_tile_reduce_kernel(BwdArgs<T> a) {
   }
 }
 
+// The reductions of one row chunk in one launch: the first blocks sum the
+// pair-bias slabs (eight values per thread), the rest the dQ partials of the
+// key ranges (eight channels per thread; none with a single key range).
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs<T> a, unsigned dbias_blocks) {
+  if (blockIdx.x < dbias_blocks)
+    dbias_tile_reduce(a, (long long)blockIdx.x * blockDim.x + threadIdx.x);
+  else
+    dq_sum(a, (long long)(blockIdx.x - dbias_blocks) * blockDim.x + threadIdx.x);
+}
+
+template <typename T>
+hipError_t launch_bwd_reduce(const BwdArgs<T>& a, hipStream_t st) {
+  const Geo& G = a.geo;
+  const long long nt = (G.n + TILE - 1) / TILE;
+  const long long dbias_threads = (long long)G.H * nt * nt * 128;
+  const long long dq_threads = a.nsplit > 1 ? (long long)G.n_rows * G.H * G.n * C / 8 : 0;
+  const unsigned db_blocks = (unsigned)((dbias_threads + 255) / 256);
+  const unsigned dq_blocks = (unsigned)((dq_threads + 255) / 256);
+  hipLaunchKernelGGL((bwd_reduce_kernel<T>), dim3(db_blocks + dq_blocks), dim3(256), 0, st, a, db_blocks);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 template <typename T> size_t tile_smem(int kpw) { return TileSmem<T>::total(kpw); }
 
-template <typename T, int KPW>
-hipError_t launch_bwd_tile(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
+// Preprocessing of every row of the call (dA, dgate, D) and the prepared bias
+// tiles; the row chunks' main kernels then read their rows of dA and D.
+template <typename T>
+hipError_t launch_bwd_prep(const BwdArgs<T>& a, hipStream_t st) {
   const Geo& G = a.geo;
   const int nt = (G.n + TILE - 1) / TILE;
-  hipError_t e;
-  if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
   const int pre_threads = G.n * G.H * 4;  // per row
   hipLaunchKernelGGL((bwd_pre_vec_kernel<T>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
                      dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
-  hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
-                     G, a.bias, a.bias_prep);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)bwd_tile_kernel<T, KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024);
-    if (e != hipSuccess) return e;
-    attr_set = true;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if constexpr (sizeof(T) == 2) {
+    return launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st);
+  } else {
+    const long long prep_threads = (long long)G.H * nt * nt * 64 + 64;
+    hipLaunchKernelGGL((bwd_bias_prep_kernel<T>), dim3((unsigned)((prep_threads + 255) / 256)), dim3(256), 0, st,
+                       G, a.bias, a.bias_prep);
+    return hipGetLastError();
   }
+}
+
+// Main kernel and reductions of one row chunk.  ev (optional): entries 1, 2
+// and 3 are recorded before the main kernel, before the reductions and after
+// them (entry 0, before the preprocessing, belongs to the caller).
+template <typename T, int KPW>
+hipError_t launch_bwd_tile_chunk(const BwdArgs<T>& a, hipStream_t st, hipEvent_t* ev) {
+  const Geo& G = a.geo;
+  hipError_t e;
+  if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
+  // set on every launch (per device, no process-wide state)
+  e = hipFuncSetAttribute((const void*)bwd_tile_kernel<T, KPW>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)TileSmem<T>::total(KPW));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_tile_kernel<T, KPW>), dim3(a.nsplit * G.n_rows * G.H), dim3(256), TileSmem<T>::total(KPW),
                      st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  const long long red_threads = (long long)G.H * nt * nt * 128;
-  hipLaunchKernelGGL((dbias_tile_reduce_kernel<T>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.nsplit > 1) {
-    const long long sum_threads = (long long)G.n_rows * G.H * G.n * C / 8;
-    hipLaunchKernelGGL((dq_sum_kernel<T>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if ((e = launch_bwd_reduce(a, st)) != hipSuccess) return e;
   if (ev && ev[3] && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
-
 size_t group_smem(int kpw) { return GroupSmem<BF16_GROUP_ROWS>::total(kpw); }
 
 template <int KPW>
-hipError_t launch_bwd_group(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* ev) {
+hipError_t launch_bwd_group_chunk(const BwdArgs<bf16>& a, hipStream_t st, hipEvent_t* ev) {
   const Geo& G = a.geo;
-  const int nt = (G.n + TILE - 1) / TILE;
   hipError_t e;
-  if (ev && ev[0] && (e = hipEventRecord(ev[0], st)) != hipSuccess) return e;
-  const int pre_threads = G.n * G.H * 4;  // per row
-  hipLaunchKernelGGL((bwd_pre_vec_kernel<bf16>), dim3((unsigned)((pre_threads + 255) / 256), (unsigned)G.n_rows),
-                     dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if ((e = launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st)) != hipSuccess) return e;
   if (ev && ev[1] && (e = hipEventRecord(ev[1], st)) != hipSuccess) return e;
-  static bool attr_set = false;
-  if (!attr_set) {
-    e = hipFuncSetAttribute((const void*)bwd_group_kernel<BF16_GROUP_ROWS, KPW>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)GroupSmem<BF16_GROUP_ROWS>::total(KPW));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // set on every launch (per device, no process-wide state)
+  e = hipFuncSetAttribute((const void*)bwd_group_kernel<BF16_GROUP_ROWS, KPW>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)GroupSmem<BF16_GROUP_ROWS>::total(KPW));
+  if (e != hipSuccess) return e;
   const int ngroups = (G.n_rows + BF16_GROUP_ROWS - 1) / BF16_GROUP_ROWS;
   hipLaunchKernelGGL((bwd_group_kernel<BF16_GROUP_ROWS, KPW>), dim3(a.nsplit * ngroups * G.H), dim3(512),
                      GroupSmem<BF16_GROUP_ROWS>::total(KPW), st, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (ev && ev[2] && (e = hipEventRecord(ev[2], st)) != hipSuccess) return e;
-  const long long red_threads = (long long)G.H * nt * nt * 128;
-  hipLaunchKernelGGL((dbias_tile_reduce_kernel<bf16>), dim3((unsigned)((red_threads + 255) / 256)), dim3(256), 0, st,
-                     a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.nsplit > 1) {
-    const long long sum_threads = (long long)G.n_rows * G.H * G.n * C / 8;
-    hipLaunchKernelGGL((dq_sum_kernel<bf16>), dim3((unsigned)((sum_threads + 255) / 256)), dim3(256), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if ((e = launch_bwd_reduce(a, st)) != hipSuccess) return e;
   if (ev && ev[3] && (e = hipEventRecord(ev[3], st)) != hipSuccess) return e;
   return hipSuccess;
 }
 
-template hipError_t launch_bwd_group<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_group<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
-
-template hipError_t launch_bwd_tile<float, 1>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
-template hipError_t launch_bwd_tile<float, 2>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_prep<bf16>(const BwdArgs<bf16>&, hipStream_t);
+template hipError_t launch_bwd_prep<float>(const BwdArgs<float>&, hipStream_t);
+template hipError_t launch_bwd_group_chunk<1>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_group_chunk<2>(const BwdArgs<bf16>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile_chunk<float, 1>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
+template hipError_t launch_bwd_tile_chunk<float, 2>(const BwdArgs<float>&, hipStream_t, hipEvent_t*);
 template size_t tile_smem<float>(int);
 
 }  // namespace tri

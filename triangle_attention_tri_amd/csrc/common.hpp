@@ -353,6 +353,12 @@ template <typename T> struct BwdArgs {
   int slab_rows;     // row slabs of dS tiles the dbias reduction sums (rows, or row groups)
   int slab_e;        // slab tile layout [16 / slab_e parts][64 lanes][slab_e values]
   const int8_t* attn_res;  // optional (bf16 runs): rounding-residual codes of attn from the forward; null = none
+  // Row chunks.  A call's rows are processed in chunks (each a row slice with
+  // its own partials in the workspace); the pair-bias gradient is carried from
+  // chunk to chunk as an fp32 running sum in the reduction's own element order.
+  float* dbias_acc;  // workspace: the running sum (unused when one chunk covers the call)
+  int acc_first;     // this chunk starts the sum (no running sum to read)
+  int acc_last;      // this chunk ends it (round and write dbias instead of the running sum)
 };
 
 // 16 consecutive floats (64 bytes, 16-byte aligned) as one accumulator tile's
