@@ -114,6 +114,30 @@ int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending,
                  void *out, void *attn_saved, float *lse,
                  void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
 
+/*
+ * tri_attn_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments, layouts, results and errors are those of
+ * tri_attn_fwd, bit for bit; the scratch the forward needs (the prepared bias
+ * tiles, tri_attn_fwd_workspace_size bytes) comes from a fixed device array of
+ * tri_attn_fwd_noalloc_max_bytes() bytes (16 MiB) inside the library, one per
+ * device, held until the process ends.  Calls whose scratch would exceed it
+ * return TRI_ATTN_EWORKSPACE before any device call (h = 4 fits up to
+ * n = 1024).  The call allocates nothing: on the first call on a device it
+ * looks up that device's copy of the array (TRI_ATTN_EHIP if that fails).
+ * Every call on one device shares that device's array and leaves its contents
+ * behind (the forward rewrites every byte it reads), so calls that overlap on
+ * one device (different streams, different host threads without ordering)
+ * race on it and must not be issued.
+ */
+int tri_attn_fwd_noalloc(int n_rows, int n, int h, int c, int dtype, int ending,
+                         const void *q, const void *k, const void *v, const void *bias,
+                         const void *gate, const uint8_t *mask,
+                         void *out, void *attn_saved, float *lse, tri_attn_stream_t stream);
+
+/* Size in bytes of tri_attn_fwd_noalloc's fixed scratch array. */
+size_t tri_attn_fwd_noalloc_max_bytes(void);
+
 /* Bytes of device workspace tri_attn_bwd needs for these sizes (0 on bad args).
  * The backward processes the call's rows in consecutive chunks of
  * tri_attn_bwd_chunk_rows rows that reuse one workspace (the gradient reaching

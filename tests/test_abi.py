@@ -150,6 +150,19 @@ def test_backward_chunks(lib):
     assert lib.tri_attn_bwd_workspace_size(n, n, 4, 32, ta.BF16) <= n * 4 * n * (32 * 2 + 4) + 700_000_000
 
 
+def test_noalloc_forward_limits(lib):
+    """tri_attn_fwd_noalloc rejects, before any device call, sizes whose scratch exceeds its fixed array and the
+    forward's usual argument errors."""
+    assert lib.tri_attn_fwd_noalloc_max_bytes() == 16 << 20
+    p = fake_ptr(0x100000)
+    args = lambda n, dt=ta.BF16, c=32, ptr=p: (n, n, 4, c, dt, 0, ptr, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr,  # noqa
+                                               None)
+    assert lib.tri_attn_fwd_noalloc(*args(1100)) == EWORKSPACE      # h * ceil(n/32)^2 * 4 KiB > 16 MiB
+    assert lib.tri_attn_fwd_noalloc(*args(64, c=16)) == EUNSUPPORTED
+    assert lib.tri_attn_fwd_noalloc(*args(64, dt=7)) == EINVAL
+    assert lib.tri_attn_fwd_noalloc(*args(64, ptr=fake_ptr(0x100008))) == EINVAL
+
+
 def test_binding_rejects_bad_inputs():
     q = torch.zeros((4, 2, 4, 32), dtype=torch.float16)
     with pytest.raises(TypeError):

@@ -57,6 +57,9 @@ def load():
     lib.tri_attn_bwd_chunk_rows.restype = i
     lib.tri_attn_bwd.argtypes = [i, i, i, i, i, i] + [vp] * 14 + [vp, sz, vp]
     lib.tri_attn_bwd.restype = i
+    lib.tri_attn_fwd_noalloc.argtypes = [i, i, i, i, i, i] + [vp] * 9 + [vp]
+    lib.tri_attn_fwd_noalloc.restype = i
+    lib.tri_attn_fwd_noalloc_max_bytes.restype = sz
     lib.tri_attn_fwd_rc.argtypes = [i, i, i, i, i, i] + [vp] * 11 + [sz, vp]
     lib.tri_attn_fwd_rc.restype = i
     lib.tri_attn_bwd_rc.argtypes = [i, i, i, i, i, i] + [vp] * 15 + [vp, sz, vp]

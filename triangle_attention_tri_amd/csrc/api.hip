@@ -359,6 +359,25 @@ int tri_attn_fwd(int n_rows, int n, int h, int c, int dtype, int ending, const v
                   workspace, workspace_bytes, (hipStream_t)stream);
 }
 
+int tri_attn_fwd_noalloc(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
+                         const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
+                         void* attn_saved, float* lse, tri_attn_stream_t stream) {
+  // every check that needs no device comes first: a size beyond the scratch is rejected before any HIP call
+  int st = check_common(n_rows, n, h, c, dtype, ending);
+  if (st != TRI_ATTN_OK) return st;
+  const void* req[] = {q, k, v, bias, gate, out, attn_saved, lse};
+  for (const void* p : req)
+    if (p == nullptr || !aligned16(p)) return TRI_ATTN_EINVAL;
+  const size_t need = align256(fwd_workspace_bytes(n, h));
+  if (need > FWD_NOALLOC_SCRATCH_BYTES) return TRI_ATTN_EWORKSPACE;
+  void* scratch = nullptr;
+  if (fwd_noalloc_scratch(&scratch) != hipSuccess) return TRI_ATTN_EHIP;
+  return fwd_impl(n_rows, n, h, c, dtype, ending, q, k, v, bias, gate, mask, out, attn_saved, nullptr, lse, scratch,
+                  FWD_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
+}
+
+size_t tri_attn_fwd_noalloc_max_bytes(void) { return FWD_NOALLOC_SCRATCH_BYTES; }
+
 int tri_attn_fwd_rc(int n_rows, int n, int h, int c, int dtype, int ending, const void* q, const void* k,
                     const void* v, const void* bias, const void* gate, const uint8_t* mask, void* out,
                     void* attn_saved, int8_t* attn_residual, float* lse, void* workspace, size_t workspace_bytes,

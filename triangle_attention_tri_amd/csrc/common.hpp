@@ -317,6 +317,11 @@ template <typename T> struct FwdArgs {
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;
+// Size of the fixed scratch array of the no-allocation forward (the prepared
+// bias tiles, h * ceil(n / 32)^2 * 4 KiB at most: h = 4 up to n = 1024).
+constexpr size_t FWD_NOALLOC_SCRATCH_BYTES = (size_t)16 << 20;
+// The calling device's copy of that array (looked up once per device).
+hipError_t fwd_noalloc_scratch(void** out);
 constexpr int BF16_GROUP_ROWS = 4;  // rows per workgroup of the bf16 backward (2 or 4)
 
 // dQ partials of the key ranges: per (range, row, h) a block of whole 32-query

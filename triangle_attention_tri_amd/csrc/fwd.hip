@@ -27,6 +27,7 @@
 // The N^2 x N logit tensor never leaves the chip (MegaFold explainer,
 // EvoFlash-3D paragraph: the cubic interaction map is produced tile by tile in
 // fast on-chip memory and discarded).
+#include <mutex>
 #include <type_traits>
 
 #include "common.hpp"
@@ -340,6 +341,37 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void 
 size_t fwd_workspace_bytes(int n, int h) {
   const size_t nt = (size_t)(n + TILE - 1) / TILE;
   return (size_t)h * nt * nt * 1024 * sizeof(float);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation forward (tri_attn_fwd_noalloc): the prepared
+// bias tiles live in this fixed device array instead of a caller workspace.
+// Each device holds its own copy until the process ends; its address is looked
+// up once per device (with that device current) and kept, and only that
+// address is passed to kernels: the array's name is a host-side stand-in.
+static __device__ __align__(256) unsigned char scratch[FWD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t fwd_noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 template <typename T, int R>
