@@ -25,7 +25,8 @@ Weights use the (out, in) convention of a linear layer: w_in [4c + c_z, c_z]
 holds the rows of W_ap, W_ag, W_bp, W_bg (c rows each) and W_g (c_z rows), in
 that order; w_out [c_z, c].  LayerNorms use the biased variance and eps = 1e-5.
 Every step is a plain numpy float64 expression in the order written above
-(matmul, sum and einsum as library primitives), with no blocking or fusion.
+(matmul and sum as library primitives; the contraction over the third token is
+one matrix product per channel), with no blocking or fusion.
 """
 from __future__ import annotations
 
@@ -70,11 +71,23 @@ def split_w_in(w_in, c):
     return w_in[:c], w_in[c:2 * c], w_in[2 * c:3 * c], w_in[3 * c:4 * c], w_in[4 * c:]
 
 
+def _cf(x):
+    """[n, n, c] -> channel-first [c, n, n] copy (x_cf[c, r, s] = x[r, s, c])."""
+    return np.ascontiguousarray(np.transpose(x, (2, 0, 1)))
+
+
+def _pl(x):
+    """channel-first [c, n, n] -> [n, n, c]."""
+    return np.ascontiguousarray(np.transpose(x, (1, 2, 0)))
+
+
 def contract(a, b, incoming):
-    """t_ij = sum_k a_ik b_jk (outgoing) or sum_k a_ki b_kj (incoming), per channel."""
+    """t_ij = sum_k a_ik b_jk (outgoing) or sum_k a_ki b_kj (incoming), per channel, as one matrix product per
+    channel: T_c = A_c B_c^T, or A_c^T B_c for incoming edges (A_c[r, s] = a[r, s, c])."""
+    ac, bc = _cf(a), _cf(b)
     if incoming:
-        return np.einsum("kic,kjc->ijc", a, b)
-    return np.einsum("ikc,jkc->ijc", a, b)
+        return _pl(np.matmul(np.transpose(ac, (0, 2, 1)), bc))
+    return _pl(np.matmul(ac, np.transpose(bc, (0, 2, 1))))
 
 
 def trimul_fwd(z, gamma_in, beta_in, w_in, gamma_out, beta_out, w_out, incoming=False, eps=EPS):
@@ -111,13 +124,15 @@ def trimul_bwd(z, gamma_in, beta_in, w_in, gamma_out, beta_out, w_out, dy, incom
     dw_out = du.reshape(-1, cz).T @ f["tl"].reshape(-1, c)
     dtl = du @ w_out
     dt, dgamma_out, dbeta_out = layer_norm_bwd(dtl, f["t_n"], f["rstd_out"], gamma_out)
-    # t = contract(a, b)
+    # t = contract(a, b), per channel: outgoing T = A B^T gives dA = dT B, dB = dT^T A;
+    # incoming T = A^T B gives dA = B dT^T, dB = A dT
+    ac, bc, dtc = _cf(f["a"]), _cf(f["b"]), _cf(dt)
     if incoming:
-        da = np.einsum("ijc,kjc->kic", dt, f["b"])   # t_ij = sum_k a_ki b_kj
-        db = np.einsum("ijc,kic->kjc", dt, f["a"])
+        da = _pl(np.matmul(bc, np.transpose(dtc, (0, 2, 1))))
+        db = _pl(np.matmul(ac, dtc))
     else:
-        da = np.einsum("ijc,jkc->ikc", dt, f["b"])   # t_ij = sum_k a_ik b_jk
-        db = np.einsum("ijc,ikc->jkc", dt, f["a"])
+        da = _pl(np.matmul(dtc, bc))
+        db = _pl(np.matmul(np.transpose(dtc, (0, 2, 1)), ac))
     # gates: a = s(ag) ap, b = s(bg) bp, g = s(gp)
     sa, sb = sigmoid(f["ag"]), sigmoid(f["bg"])
     dap = da * sa
