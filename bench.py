@@ -244,6 +244,95 @@ def time_chunked(lib, hip, dev, stream, n, steps, warmup, rows_list=(768, 128, 3
     return res
 
 
+def time_trimul(lib, hip, dev, stream, n, steps, warmup):
+    """Triangular multiplicative update at n x n x 128 (bf16, c = 128), forward + backward, both edge directions.
+
+    A step is tri_mul_fwd + tri_mul_bwd with every buffer allocated before timing.  K bare steps give the step
+    time; K more through the profiled entry points give the split into the input side, the contraction over the
+    third token (forward: T_c = A_c B_c^T; backward: dA_c = dT_c B_c and dB_c = dT_c^T A_c) and the output side.
+    Each contraction is one GEMM launch of 2 n^3 c flops; its roofline is that count over its event-timed launch.
+    """
+    import torch
+
+    import triangle_attention_tri_amd as ta
+    from triangle_attention_tri_amd import inputs
+    cz = c = 128
+    x = {k: v.to(dev) for k, v in inputs.trimul_inputs(n, seed=n).items()}
+    names = ta.TRIMUL_PARAMS
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    sz = ctypes.c_size_t
+    saved_bytes = lib.tri_mul_saved_size(n, cz, c, ta.BF16)
+    ws_bytes = lib.tri_mul_workspace_size(n, cz, c, ta.BF16)
+    saved = torch.empty(saved_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y, dz = torch.empty_like(x["z"]), torch.empty_like(x["z"])
+    grads = [torch.empty_like(x[k]) for k in names]
+    f = ctypes.c_float(1e-5)
+    vp = ctypes.c_void_p
+    lib.tri_mul_fwd_profiled.argtypes = list(lib.tri_mul_fwd.argtypes) + [vp]
+    lib.tri_mul_fwd_profiled.restype = ctypes.c_int
+    lib.tri_mul_bwd_profiled.argtypes = list(lib.tri_mul_bwd.argtypes) + [vp]
+    lib.tri_mul_bwd_profiled.restype = ctypes.c_int
+    fev, bev = (ctypes.c_void_p * 4)(), (ctypes.c_void_p * 5)()
+
+    def step(inc, fe=None, be=None):
+        fa = (n, cz, c, ta.BF16, inc, P(x["z"]), *[P(x[k]) for k in names], f, P(y), P(saved), sz(saved_bytes),
+              stream)
+        ba = (n, cz, c, ta.BF16, inc, P(x["z"]), *[P(x[k]) for k in names], f, P(saved), sz(saved_bytes),
+              P(x["dy"]), P(dz), *[P(t) for t in grads], P(ws), sz(ws_bytes), stream)
+        if fe is None:
+            assert lib.tri_mul_fwd(*fa) == 0
+            assert lib.tri_mul_bwd(*ba) == 0
+            return
+        for i in range(4):
+            fev[i] = fe[i]
+        for i in range(5):
+            bev[i] = be[i]
+        assert lib.tri_mul_fwd_profiled(*fa, ctypes.cast(fev, vp)) == 0
+        assert lib.tri_mul_bwd_profiled(*ba, ctypes.cast(bev, vp)) == 0
+
+    contraction = 2.0 * n ** 3 * c
+    pairs = n * n
+    linear = 2.0 * pairs * cz * (4 * c + cz) * 3 + 2.0 * pairs * c * cz * 3
+    out = {"workload": f"trimul_N{n}_cz{cz}_c{c}_bf16", "flops_per_step": 3 * contraction + linear,
+           "contraction_flops_per_step": 3 * contraction}
+    for inc in (0, 1):
+        for _ in range(warmup):
+            step(inc)
+        t0, t1 = hip.event(), hip.event()
+        torch.cuda.synchronize()
+        hip.record(t0, stream)
+        for _ in range(steps):
+            step(inc)
+        hip.record(t1, stream)
+        torch.cuda.synchronize()
+        ms = hip.ms(t0, t1) / steps
+        st = dict(front_fwd=0.0, contract_fwd=0.0, back_fwd=0.0, back_bwd=0.0, contract_da=0.0, contract_db=0.0,
+                  front_bwd=0.0)
+        for _ in range(steps):
+            fe = [hip.event() for _ in range(4)]
+            be = [hip.event() for _ in range(5)]
+            step(inc, fe, be)
+            torch.cuda.synchronize()
+            for key, (a, b) in zip(("front_fwd", "contract_fwd", "back_fwd"), ((fe[0], fe[1]), (fe[1], fe[2]),
+                                                                              (fe[2], fe[3]))):
+                st[key] += hip.ms(a, b) / steps
+            for key, (a, b) in zip(("back_bwd", "contract_da", "contract_db", "front_bwd"),
+                                   ((be[0], be[1]), (be[1], be[2]), (be[2], be[3]), (be[3], be[4]))):
+                st[key] += hip.ms(a, b) / steps
+        launch = {k: st[k] for k in ("contract_fwd", "contract_da", "contract_db")}
+        kmax = max(launch, key=launch.get)
+        ach = contraction / (launch[kmax] * 1e-3) / 1e12
+        out["incoming" if inc else "outgoing"] = {
+            "ms_per_step": round(ms, 4), "tflops": round(out["flops_per_step"] / (ms * 1e-3) / 1e12, 2),
+            "stages_ms": {k: round(v, 4) for k, v in st.items()},
+            "contraction_roofline": {"kernel": "gemm_kernel (per-channel contraction, " + kmax + ")",
+                                     "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                                     "launch_ms": round(launch[kmax], 4)}}
+    return out
+
+
 class AttnCase:
     """One attention workload resident on the GPU: seeded inputs, outputs, workspaces and the C ABI calls of a
     step (tri_attn_fwd + tri_attn_bwd, or the residual-compensated pair)."""
@@ -426,6 +515,8 @@ def main():
     ap.add_argument("--no-block", action="store_true",
                     help="skip the LayerNorm + projection + attention + output-linear block timing")
     ap.add_argument("--no-configs", action="store_true", help="skip the smaller configurations")
+    ap.add_argument("--no-trimul", action="store_true", help="skip the triangular multiplicative update timing")
+    ap.add_argument("--trimul-only", action="store_true", help="time only the triangular multiplicative update")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -453,6 +544,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.trimul_only:
+        print(json.dumps(time_trimul(lib, hip, dev, stream, args.n, args.steps, args.warmup)), flush=True)
+        return
 
     if args.config is not None:
         for line in time_configs(lib, hip, dev, stream, [args.config], args.steps, args.warmup):
@@ -502,6 +597,7 @@ def main():
     chunked = None if args.no_chunked else time_chunked(lib, hip, dev, stream, n, 3, 1)
     configs = None if args.no_configs else time_configs(lib, hip, dev, stream, sorted(CONFIGS),
                                                         max(5, args.steps // 2), 3)
+    trimul = None if args.no_trimul else time_trimul(lib, hip, dev, stream, n, max(3, args.steps // 4), 2)
 
     cpu = None
     if rank == 0 and args.cpu_rows > 0:
@@ -519,6 +615,7 @@ def main():
         "residual_compensated_ms_per_step": None if rc_ms is None else round(rc_ms, 4),
         "roofline": roofline,
         "configs": configs,
+        "trimul": trimul,
         "block": block,
         "chunked_block_fwd": chunked,
         "cpu_baseline": cpu,

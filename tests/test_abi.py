@@ -18,14 +18,17 @@ import triangle_attention_tri_amd as ta
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tri_attn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, -1, -2, -3, -4
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tri_attn_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(tri_(?:attn|mul)_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -38,7 +41,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = declared_functions()
-    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_workspace_size"} <= set(names)
+    assert {"tri_attn_fwd", "tri_attn_bwd", "tri_attn_bwd_workspace_size", "tri_mul_fwd", "tri_mul_bwd"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in tri_attn.h but not exported"
 
@@ -349,3 +352,27 @@ def test_projection_binding_shape_checks():
         ta.out_proj_fwd(torch.zeros(n, n, h, c - 1, **bf), w_o)
     with pytest.raises(ValueError, match="dy must have shape"):
         ta.out_proj_bwd(torch.zeros(n, n, h, c, **bf), w_o, torch.zeros(n, n - 1, cz, **bf))
+
+
+def test_trimul_validation(lib):
+    """tri_mul_* reject bad arguments before any device call."""
+    p = fake_ptr(0x100000)
+    big = ctypes.c_size_t(1 << 40)
+    f = ctypes.c_float
+
+    def fwd(n=64, cz=128, c=128, dt=ta.BF16, inc=0, ptr=p, eps=1e-5, saved=p, saved_bytes=big):
+        return lib.tri_mul_fwd(n, cz, c, dt, inc, ptr, p, p, p, p, p, p, f(eps), p, saved, saved_bytes, None)
+
+    def bwd(n=64, ws=p, ws_bytes=big, saved_bytes=big, ptr=p):
+        return lib.tri_mul_bwd(n, 128, 128, ta.BF16, 0, ptr, p, p, p, p, p, p, f(1e-5), p, saved_bytes, p,
+                               p, p, p, p, p, p, p, ws, ws_bytes, None)
+    assert lib.tri_mul_saved_size(64, 128, 128, ta.BF16) > 0 and lib.tri_mul_workspace_size(64, 128, 128, ta.BF16) > 0
+    assert lib.tri_mul_saved_size(64, 64, 128, ta.BF16) == 0 and lib.tri_mul_saved_size(0, 128, 128, ta.BF16) == 0
+    assert fwd(n=0) == EINVAL and fwd(inc=2) == EINVAL and fwd(dt=5) == EINVAL
+    assert fwd(cz=64) == EUNSUPPORTED and fwd(c=96) == EUNSUPPORTED and fwd(dt=ta.F32) == EUNSUPPORTED
+    assert fwd(n=5000) == EUNSUPPORTED
+    assert fwd(eps=0.0) == EINVAL and fwd(ptr=fake_ptr(0x100008)) == EINVAL and fwd(ptr=None) == EINVAL
+    assert fwd(saved=None) == EWORKSPACE and fwd(saved_bytes=ctypes.c_size_t(100)) == EWORKSPACE
+    assert fwd(saved=fake_ptr(0x100000 + 16)) == EINVAL
+    assert bwd(ws=None) == EWORKSPACE and bwd(saved_bytes=ctypes.c_size_t(10)) == EWORKSPACE
+    assert bwd(ptr=fake_ptr(0x100004)) == EINVAL

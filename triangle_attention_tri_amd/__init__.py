@@ -21,8 +21,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["fwd", "bwd", "workspace_size", "bwd_chunk_rows", "fwd_workspace_size", "max_n", "TriAttnFunction", "tri_attn", "lib_path",
-           "load", "ln_proj_fwd", "ln_proj_bwd", "out_proj_fwd", "out_proj_bwd", "block_fwd", "block_bwd"]
+__all__ = ["fwd", "bwd", "workspace_size", "bwd_chunk_rows", "fwd_workspace_size", "max_n", "TriAttnFunction",
+           "tri_attn", "lib_path",
+           "load", "ln_proj_fwd", "ln_proj_bwd", "out_proj_fwd", "out_proj_bwd", "block_fwd", "block_bwd",
+           "trimul_fwd", "trimul_bwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libtri_attn.so")
@@ -83,6 +85,14 @@ def load():
     lib.tri_attn_block_chunk_rows.restype = i
     lib.tri_attn_block_fwd_chunked.argtypes = [i] * 6 + [vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tri_attn_block_fwd_chunked.restype = i
+    lib.tri_mul_saved_size.argtypes = [i] * 4
+    lib.tri_mul_saved_size.restype = sz
+    lib.tri_mul_workspace_size.argtypes = [i] * 4
+    lib.tri_mul_workspace_size.restype = sz
+    lib.tri_mul_fwd.argtypes = [i] * 5 + [vp] * 7 + [f, vp, vp, sz, vp]
+    lib.tri_mul_fwd.restype = i
+    lib.tri_mul_bwd.argtypes = [i] * 5 + [vp] * 7 + [f, vp, sz, vp] + [vp] * 7 + [vp, sz, vp]
+    lib.tri_mul_bwd.restype = i
     _lib = lib
     return lib
 
@@ -416,6 +426,66 @@ def block_fwd_chunked(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_c
                                         _ptr(workspace), ctypes.c_size_t(need), _stream(z.device))
     _check(st, "tri_attn_block_fwd_chunked")
     return y, int(rows_per_chunk), need
+
+
+# ---------------------------------------------------------------------------
+# Triangular multiplicative update (include/tri_mul.h): bf16, c_z = c = 128
+
+TRIMUL_PARAMS = ("gamma_in", "beta_in", "w_in", "gamma_out", "beta_out", "w_out")
+
+
+def _trimul_check(z, p):
+    import torch
+    n, n2, cz = z.shape
+    if n != n2:
+        raise ValueError("z must be [n, n, c_z]")
+    c = p["w_out"].shape[1]
+    _prep(dict(z=z, **p), torch.bfloat16, z.device)
+    for name, shape in dict(gamma_in=(cz,), beta_in=(cz,), w_in=(4 * c + cz, cz), gamma_out=(c,), beta_out=(c,),
+                            w_out=(cz, c)).items():
+        _expect(name, p[name], shape)
+    return n, cz, c
+
+
+def trimul_fwd(z, params: dict, incoming: bool = False, eps: float = 1e-5):
+    """y = triangular multiplicative update of z [n, n, c_z] (outgoing or incoming edges).
+
+    ``params`` holds gamma_in, beta_in, w_in [4c + c_z, c_z], gamma_out, beta_out, w_out [c_z, c].
+    Returns (y, saved); ``saved`` is what trimul_bwd needs.
+    """
+    import torch
+    lib = load()
+    p = {k: params[k] for k in TRIMUL_PARAMS}
+    n, cz, c = _trimul_check(z, p)
+    need = int(lib.tri_mul_saved_size(n, cz, c, BF16))
+    if need == 0:
+        _check(-2, "tri_mul_saved_size")
+    saved = torch.empty(need, dtype=torch.uint8, device=z.device)
+    y = torch.empty_like(z)
+    st = lib.tri_mul_fwd(n, cz, c, BF16, int(bool(incoming)), _ptr(z), *[_ptr(p[k]) for k in TRIMUL_PARAMS],
+                         ctypes.c_float(eps), _ptr(y), _ptr(saved), ctypes.c_size_t(need), _stream(z.device))
+    _check(st, "tri_mul_fwd")
+    return y, saved
+
+
+def trimul_bwd(z, params: dict, saved, dy, incoming: bool = False, eps: float = 1e-5, workspace=None):
+    """Returns dict(dz, dgamma_in, dbeta_in, dw_in, dgamma_out, dbeta_out, dw_out)."""
+    import torch
+    lib = load()
+    p = {k: params[k] for k in TRIMUL_PARAMS}
+    n, cz, c = _trimul_check(z, p)
+    _prep(dict(dy=dy), torch.bfloat16, z.device)
+    _expect("dy", dy, tuple(z.shape))
+    need = int(lib.tri_mul_workspace_size(n, cz, c, BF16))
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+    out = dict(dz=torch.empty_like(z), **{"d" + k: torch.empty_like(p[k]) for k in TRIMUL_PARAMS})
+    st = lib.tri_mul_bwd(n, cz, c, BF16, int(bool(incoming)), _ptr(z), *[_ptr(p[k]) for k in TRIMUL_PARAMS],
+                         ctypes.c_float(eps), _ptr(saved), ctypes.c_size_t(saved.numel()), _ptr(dy), _ptr(out["dz"]),
+                         *[_ptr(out["d" + k]) for k in TRIMUL_PARAMS], _ptr(workspace),
+                         ctypes.c_size_t(workspace.numel()), _stream(z.device))
+    _check(st, "tri_mul_bwd")
+    return out
 
 
 def __getattr__(name):

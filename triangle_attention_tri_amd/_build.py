@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libtri_attn.so")
 SOURCES = sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
-DEPS = SOURCES + sorted(glob.glob(os.path.join(PKG, "csrc", "*.hpp"))) + [os.path.join(ROOT, "include", "tri_attn.h")]
+DEPS = SOURCES + sorted(glob.glob(os.path.join(PKG, "csrc", "*.hpp"))) + sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions stay off: the kernels are written for scalar fp32 VALU.
 # MFMA accumulators stay in VGPR form: the AGPR form makes the compiler shuttle

@@ -663,3 +663,111 @@ int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Triangular multiplicative update (include/tri_mul.h).
+#include "../../include/tri_mul.h"
+#include "trimul.hpp"
+
+namespace {
+
+int check_trimul(int n, int cz, int c, int dtype, int incoming) {
+  if (n < 1 || cz < 1 || c < 1) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_F32 && dtype != TRI_ATTN_BF16) return TRI_ATTN_EINVAL;
+  if (incoming != 0 && incoming != 1) return TRI_ATTN_EINVAL;
+  if (dtype != TRI_ATTN_BF16 || cz != tri::tm::CZ || c != tri::tm::CH || n > 4096) return TRI_ATTN_EUNSUPPORTED;
+  return TRI_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tri_mul_saved_size(int n, int cz, int c, int dtype) {
+  return check_trimul(n, cz, c, dtype, 0) == TRI_ATTN_OK ? tri::trimul_saved_bytes(n) : 0;
+}
+
+size_t tri_mul_workspace_size(int n, int cz, int c, int dtype) {
+  return check_trimul(n, cz, c, dtype, 0) == TRI_ATTN_OK ? tri::trimul_workspace_bytes(n) : 0;
+}
+
+static int trimul_fwd_impl(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                           const void* ln_in_beta, const void* w_in, const void* ln_out_gamma,
+                           const void* ln_out_beta, const void* w_out, float ln_eps, void* y, void* saved,
+                           size_t saved_bytes, tri_attn_stream_t stream, hipEvent_t* ev) {
+  int st = check_trimul(n, cz, c, dtype, incoming);
+  if (st != TRI_ATTN_OK) return st;
+  if (!(ln_eps > 0.0f) || !(ln_eps < 1.0f)) return TRI_ATTN_EINVAL;
+  const void* a16[] = {z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta, w_out, y};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  if ((st = check_ws(saved, saved_bytes, tri::trimul_saved_bytes(n))) != TRI_ATTN_OK) return st;
+  const tri::TmParams w{(const bf16*)ln_in_gamma, (const bf16*)ln_in_beta, (const bf16*)w_in,
+                        (const bf16*)ln_out_gamma, (const bf16*)ln_out_beta, (const bf16*)w_out};
+  return hip_status(tri::trimul_fwd(n, incoming, w, (const bf16*)z, (bf16*)y, saved, ln_eps, (hipStream_t)stream,
+                                    ev));
+}
+
+int tri_mul_fwd(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                const void* ln_in_beta, const void* w_in, const void* ln_out_gamma, const void* ln_out_beta,
+                const void* w_out, float ln_eps, void* y, void* saved, size_t saved_bytes, tri_attn_stream_t stream) {
+  return trimul_fwd_impl(n, cz, c, dtype, incoming, z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta,
+                         w_out, ln_eps, y, saved, saved_bytes, stream, nullptr);
+}
+
+int tri_mul_fwd_profiled(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                         const void* ln_in_beta, const void* w_in, const void* ln_out_gamma, const void* ln_out_beta,
+                         const void* w_out, float ln_eps, void* y, void* saved, size_t saved_bytes,
+                         tri_attn_stream_t stream, tri_attn_event_t* events) {
+  if (events == nullptr) return TRI_ATTN_EINVAL;
+  return trimul_fwd_impl(n, cz, c, dtype, incoming, z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta,
+                         w_out, ln_eps, y, saved, saved_bytes, stream, (hipEvent_t*)events);
+}
+
+static int trimul_bwd_impl(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                           const void* ln_in_beta, const void* w_in, const void* ln_out_gamma,
+                           const void* ln_out_beta, const void* w_out, float ln_eps, const void* saved,
+                           size_t saved_bytes, const void* dy, void* dz, void* dln_in_gamma, void* dln_in_beta,
+                           void* dw_in, void* dln_out_gamma, void* dln_out_beta, void* dw_out, void* workspace,
+                           size_t workspace_bytes, tri_attn_stream_t stream, hipEvent_t* ev) {
+  int st = check_trimul(n, cz, c, dtype, incoming);
+  if (st != TRI_ATTN_OK) return st;
+  if (!(ln_eps > 0.0f) || !(ln_eps < 1.0f)) return TRI_ATTN_EINVAL;
+  const void* a16[] = {z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta, w_out, dy, dz,
+                       dln_in_gamma, dln_in_beta, dw_in, dln_out_gamma, dln_out_beta, dw_out};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  if (saved == nullptr || saved_bytes < tri::trimul_saved_bytes(n)) return TRI_ATTN_EWORKSPACE;
+  if (((uintptr_t)saved & 255u) != 0) return TRI_ATTN_EINVAL;
+  if ((st = check_ws(workspace, workspace_bytes, tri::trimul_workspace_bytes(n))) != TRI_ATTN_OK) return st;
+  const tri::TmParams w{(const bf16*)ln_in_gamma, (const bf16*)ln_in_beta, (const bf16*)w_in,
+                        (const bf16*)ln_out_gamma, (const bf16*)ln_out_beta, (const bf16*)w_out};
+  const tri::TmGrads d{(bf16*)dln_in_gamma, (bf16*)dln_in_beta, (bf16*)dw_in,
+                       (bf16*)dln_out_gamma, (bf16*)dln_out_beta, (bf16*)dw_out};
+  return hip_status(tri::trimul_bwd(n, incoming, w, (const bf16*)z, (const bf16*)dy, saved, (bf16*)dz, d,
+                                    workspace, ln_eps, (hipStream_t)stream, ev));
+}
+
+int tri_mul_bwd(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                const void* ln_in_beta, const void* w_in, const void* ln_out_gamma, const void* ln_out_beta,
+                const void* w_out, float ln_eps, const void* saved, size_t saved_bytes, const void* dy, void* dz,
+                void* dln_in_gamma, void* dln_in_beta, void* dw_in, void* dln_out_gamma, void* dln_out_beta,
+                void* dw_out, void* workspace, size_t workspace_bytes, tri_attn_stream_t stream) {
+  return trimul_bwd_impl(n, cz, c, dtype, incoming, z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta,
+                         w_out, ln_eps, saved, saved_bytes, dy, dz, dln_in_gamma, dln_in_beta, dw_in, dln_out_gamma,
+                         dln_out_beta, dw_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int tri_mul_bwd_profiled(int n, int cz, int c, int dtype, int incoming, const void* z, const void* ln_in_gamma,
+                         const void* ln_in_beta, const void* w_in, const void* ln_out_gamma, const void* ln_out_beta,
+                         const void* w_out, float ln_eps, const void* saved, size_t saved_bytes, const void* dy,
+                         void* dz, void* dln_in_gamma, void* dln_in_beta, void* dw_in, void* dln_out_gamma,
+                         void* dln_out_beta, void* dw_out, void* workspace, size_t workspace_bytes,
+                         tri_attn_stream_t stream, tri_attn_event_t* events) {
+  if (events == nullptr) return TRI_ATTN_EINVAL;
+  return trimul_bwd_impl(n, cz, c, dtype, incoming, z, ln_in_gamma, ln_in_beta, w_in, ln_out_gamma, ln_out_beta,
+                         w_out, ln_eps, saved, saved_bytes, dy, dz, dln_in_gamma, dln_in_beta, dw_in, dln_out_gamma,
+                         dln_out_beta, dw_out, workspace, workspace_bytes, stream, (hipEvent_t*)events);
+}
+
+}  // extern "C"

@@ -121,3 +121,25 @@ def proj_grad_inputs(n: int, h: int = 4, c: int = 32, dtype=torch.bfloat16, seed
                dv=torch.randn((n, h, n, c), generator=g), dgate=torch.randn((n, n, h, c), generator=g),
                dbias=torch.randn((h, n, n), generator=g))
     return {key: t.to(dtype) for key, t in out.items()}
+
+
+def trimul_inputs(n: int, cz: int = 128, c: int = 128, dtype=torch.bfloat16, seed: int = 7) -> dict:
+    """Seeded inputs of the triangular multiplicative update.
+
+    Draw order: z [n,n,cz] ~ N(0,1); w_in [4c+cz, cz] and w_out [cz, c] ~ N(0, 1/fan_in) (standard deviation
+    1/sqrt(fan_in)); dy [n,n,cz] ~ N(0,1); then gamma_in, gamma_out ~ 1 + 0.1 N(0,1) and beta_in, beta_out ~
+    0.1 N(0,1), so that tests see the LayerNorm parameters act.  bf16 rounds every tensor (the oracle reads the
+    rounded values).
+    """
+    g = torch.Generator().manual_seed(int(seed))
+    z = torch.randn((n, n, cz), generator=g)
+    w_in = torch.randn((4 * c + cz, cz), generator=g) / cz ** 0.5
+    w_out = torch.randn((cz, c), generator=g) / c ** 0.5
+    dy = torch.randn((n, n, cz), generator=g)
+    gamma_in = 1.0 + 0.1 * torch.randn(cz, generator=g)
+    beta_in = 0.1 * torch.randn(cz, generator=g)
+    gamma_out = 1.0 + 0.1 * torch.randn(c, generator=g)
+    beta_out = 0.1 * torch.randn(c, generator=g)
+    out = dict(z=z, w_in=w_in, w_out=w_out, dy=dy, gamma_in=gamma_in, beta_in=beta_in, gamma_out=gamma_out,
+               beta_out=beta_out)
+    return {key: t.to(dtype) for key, t in out.items()}
