@@ -18,9 +18,10 @@
 // incoming edges, and the host hands the a and b weight blocks over swapped.
 //
 // Data flow (kernel frame, P = N^2 pairs p * N + q, Np = N rounded up to 128):
-//   forward   ln_in:    z -> xhat [P][128], LN statistics
-//             GEMM:     pre [P][640] = xhat . W^T      (a_p, a_g, b_p, b_g, g_pre)
-//             gate_in:  A, B [128][Np][Np] channel-major (zero padding), G = s(g_pre) [P][128]
+//   forward   front:    z -> xhat [P][128], LN statistics, and in the same
+//                       pass the projections x . W^T (a_p, a_g, b_p, b_g, g_pre)
+//                       gated into A, B [128][Np][Np] channel-major (zero
+//                       padding) and G = s(g_pre) [P][128]
 //             GEMM x128 channels: T_c = A_c B_c^T       (the cubic step: 2 N^3 c flops)
 //             ln_out:   tl = LN(T) [P][128], statistics
 //             GEMM:     u = tl . W_o^T;   gate_out: y = G * u
@@ -30,10 +31,11 @@
 //             LayerNorm parameter gradients are per-block partials summed in
 //             block order, so every result is bitwise reproducible.
 //
-// All products run through one MFMA GEMM kernel (bf16 32x32x16, fp32
-// accumulation, 128 x 128 tiles); the per-pair steps are small fused kernels
-// that also do the transposes between the pair-major and channel-major
-// layouts through LDS.
+// The products over pairs run through one MFMA GEMM kernel (bf16 32x32x16,
+// fp32 accumulation, 128 x 128 tiles); the input side's projections (K = 128)
+// run inside the fused per-pair kernels, whose MFMA outputs give the
+// channel-major layout directly.  The backward's input side recomputes the
+// projections from xhat instead of keeping them.
 #include "trimul.hpp"
 
 namespace tri {
@@ -209,91 +211,302 @@ __device__ __forceinline__ float sum4(float x) {
   return x;
 }
 
-// LayerNorm of z (caller frame) -> xhat [P][128] and statistics; 16 threads per
-// pair, 8 channels each.
-__global__ __launch_bounds__(256) void ln_in_kernel(TmArgs a) {
-  const long long t = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long pp = t >> 4;
-  const int c0 = (int)(t & 15) * 8;
-  const bool live = pp < a.P;
-  const long long ppc = live ? pp : 0;
-  const long long p = ppc / a.n, q = ppc % a.n;
-  float z[8];
-  load8f(a.z + p * a.zr + q * a.zq + c0, z);
-  float s = 0.0f;
+// ---------------------------------------------------------------------------
+// Input side, fused: LayerNorm, the five projections and the gating in one
+// pass.  A wave takes NS sets of 32 consecutive pairs (rows p0 .. p0 + NS - 1,
+// columns q0 .. q0 + 31); four waves per block cover 128 columns.  A lane
+// holds its pair's 64 of the 128 channels as the MFMA operand (channel
+// 32 kk + 16 u + 8 g + e in element e of part u of operand kk), so the
+// normalised x never leaves registers.  The weights pass through LDS in ten
+// chunks of 64 rows, double-buffered and read with whole-row loads.  They come
+// in "chunk order" (wk, written by permute_w_kernel): chunk c = rows
+// 64 c .. 64 c + 63 of wk is
+//   c < 8:  block blk = c / 4 (a, then b), channels 32 cb .. 32 cb + 31
+//           (cb = c % 4): rows 0 .. 31 the projection, 32 .. 63 its gate;
+//   c >= 8: 64 rows of the g block.
+// The backward's dpre columns use the same order, so a chunk's derivatives
+// are 128 contiguous bytes of a pair's row.  A chunk is stored as four
+// [64 rows][PITCH] sub-tiles, one per 32 input channels, so the c-map
+// operand reads are the GEMM kernel's.
+constexpr int WCH = 64;                 // weight rows per chunk
+constexpr int WSUB = WCH * PITCH;       // elements of one 32-column sub-tile of a chunk
+constexpr int NCHUNK = 10;
+
+struct WStage { V16 v[4]; };            // one thread's 4 x 16 bytes of a chunk
+__device__ __forceinline__ void w_fetch(WStage& st, const bf16* w, int c, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) s += z[i];
-  const float mean = sum16(s) * (1.0f / CZ);
-  float v = 0.0f;
+  for (int i = 0; i < 4; i++) {
+    const int idx = tid + 256 * i, row = idx >> 4, pc = idx & 15;
+    st.v[i] = *reinterpret_cast<const V16*>(w + (WCH * c + row) * CZ + 8 * pc);
+  }
+}
+__device__ __forceinline__ void w_put(const WStage& st, bf16* buf, int tid) {
 #pragma unroll
-  for (int i = 0; i < 8; i++) v += (z[i] - mean) * (z[i] - mean);
-  const float rstd = __builtin_amdgcn_rsqf(sum16(v) * (1.0f / CZ) + a.eps);
-  float gam[8], bet[8], x[8];
-  load8f(a.gamma_in + c0, gam);
-  load8f(a.beta_in + c0, bet);
+  for (int i = 0; i < 4; i++) {
+    const int idx = tid + 256 * i, row = idx >> 4, pc = idx & 15;
+    *reinterpret_cast<V16*>(buf + (pc >> 2) * WSUB + row * PITCH + 8 * (pc & 3)) = st.v[i];
+  }
+}
+// order a wave's own LDS accesses (the tiles below are private to a wave)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// 32 x 32 MFMA result -> per-wave tile [32][PITCH] (row = the lane's index l32,
+// columns mrow(g, r) = 8 s4 + 4 g + t), as bf16 of f(v)
+__device__ __forceinline__ void tile_put4(bf16* t, int l32, int g, int s4, const bf16x4& v) {
+  *reinterpret_cast<bf16x4*>(t + l32 * PITCH + 8 * s4 + 4 * g) = v;
+}
+// a tile row piece: 16 consecutive rows per instruction, 4 lanes x 16 bytes per row
+__device__ __forceinline__ V16 tile_row_piece(const bf16* t, int lane, int it) {
+  return *reinterpret_cast<const V16*>(t + ((lane >> 2) + 16 * it) * PITCH + 8 * (lane & 3));
+}
+
+template <int NS>
+__global__ __launch_bounds__(256, 2) void front_fwd_kernel(TmArgs a, const bf16* __restrict__ w) {
+  __shared__ __align__(16) bf16 sW[2][4 * WSUB];
+  __shared__ __align__(16) bf16 sT[4][32 * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long q0 = (long long)blockIdx.x * 128 + 32 * wv;
+  const long long q = q0 + l32;
+  const long long p0 = (long long)blockIdx.y * NS;
+  WStage stg;
+  w_fetch(stg, w, 0, tid);
+  Op<bf16> X[NS][4];
 #pragma unroll
-  for (int i = 0; i < 8; i++) x[i] = (z[i] - mean) * rstd * gam[i] + bet[i];
-  if (!live) return;
-  store8(a.xhat + pp * CZ + c0, x);
-  if (c0 == 0) {
-    a.mean_in[pp] = mean;
-    a.rstd_in[pp] = rstd;
+  for (int s = 0; s < NS; s++) {
+    const long long p = p0 + s;
+    const bool live = p < a.n && q < a.n;
+    const long long pp = live ? p * a.n + q : 0;
+    const bf16* zp = a.z + (live ? p * a.zr + q * a.zq : 0);
+    float x[4][2][8];
+    float sm = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        load8f(zp + 32 * kk + 16 * u + 8 * g, x[kk][u]);
+#pragma unroll
+        for (int e = 0; e < 8; e++) sm += x[kk][u][e];
+      }
+    const float mean = (sm + __shfl_xor(sm, 32)) * (1.0f / CZ);
+    float v = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+      for (int u = 0; u < 2; u++)
+#pragma unroll
+        for (int e = 0; e < 8; e++) v += (x[kk][u][e] - mean) * (x[kk][u][e] - mean);
+    const float rstd = __builtin_amdgcn_rsqf((v + __shfl_xor(v, 32)) * (1.0f / CZ) + a.eps);
+#pragma unroll
+    for (int kk = 0; kk < 4; kk++)
+#pragma unroll
+      for (int u = 0; u < 2; u++) {
+        float gam[8], bet[8];
+        load8f(a.gamma_in + 32 * kk + 16 * u + 8 * g, gam);
+        load8f(a.beta_in + 32 * kk + 16 * u + 8 * g, bet);
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          X[s][kk].f[u][e] = (bf16)(live ? (x[kk][u][e] - mean) * rstd * gam[e] + bet[e] : 0.0f);
+      }
+    if (live) {
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) store_c_op(a.xhat + pp * CZ + 32 * kk, X[s][kk], g);
+      if (g == 0) {
+        a.mean_in[pp] = mean;
+        a.rstd_in[pp] = rstd;
+      }
+    }
+  }
+  w_put(stg, sW[0], tid);
+  __syncthreads();
+  const long long np2 = (long long)a.np * a.np;
+  bf16* const tt = sT[wv];
+  for (int c = 0; c < NCHUNK; c++) {
+    if (c + 1 < NCHUNK) w_fetch(stg, w, c + 1, tid);
+    const bf16* wb = sW[c & 1];
+    if (c < 8) {
+      f32x16 ap[NS], ag[NS];
+#pragma unroll
+      for (int s = 0; s < NS; s++) ap[s] = ag[s] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        const Op<bf16> wp = lds_c_op(wb + kk * WSUB + l32 * PITCH, g);
+        const Op<bf16> wg = lds_c_op(wb + kk * WSUB + (32 + l32) * PITCH, g);
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+          ap[s] = mma32(X[s][kk], wp, ap[s]);
+          ag[s] = mma32(X[s][kk], wg, ag[s]);
+        }
+      }
+      // ap[s][r]: pair (p0 + s, q0 + mrow(g, r)), channel 32 cb + l32; the tile
+      // turns it into channel rows of 32 pairs (64 contiguous bytes each)
+      bf16* dst = ((c >> 2) ? a.B : a.A) + (long long)(32 * (c & 3)) * np2 + q0;
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; s4++) {
+          bf16x4 o;
+#pragma unroll
+          for (int t = 0; t < 4; t++) o[t] = (bf16)(sig(ag[s][4 * s4 + t]) * ap[s][4 * s4 + t]);
+          tile_put4(tt, l32, g, s4, o);
+        }
+        wave_sync();
+#pragma unroll
+        for (int it = 0; it < 2; it++)
+          *reinterpret_cast<V16*>(dst + ((lane >> 2) + 16 * it) * np2 + (p0 + s) * a.np + 8 * (lane & 3)) =
+              tile_row_piece(tt, lane, it);
+        wave_sync();
+      }
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; sub++) {
+        f32x16 gg[NS];
+#pragma unroll
+        for (int s = 0; s < NS; s++) gg[s] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < 4; kk++) {
+          const Op<bf16> wg = lds_c_op(wb + kk * WSUB + (32 * sub + l32) * PITCH, g);
+#pragma unroll
+          for (int s = 0; s < NS; s++) gg[s] = mma32(wg, X[s][kk], gg[s]);
+        }
+        // gg[s][r]: channel 64 (c - 8) + 32 sub + mrow(g, r), pair (p0 + s, q0 + l32);
+        // the tile turns it into pair rows of 32 channels
+        const int ch = 64 * (c - 8) + 32 * sub;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+#pragma unroll
+          for (int s4 = 0; s4 < 4; s4++) {
+            bf16x4 o;
+#pragma unroll
+            for (int t = 0; t < 4; t++) o[t] = (bf16)sig(gg[s][4 * s4 + t]);
+            tile_put4(tt, l32, g, s4, o);
+          }
+          wave_sync();
+          const long long p = p0 + s;
+#pragma unroll
+          for (int it = 0; it < 2; it++) {
+            const long long qq = q0 + (lane >> 2) + 16 * it;
+            const V16 v = tile_row_piece(tt, lane, it);
+            if (p < a.n && qq < a.n) *reinterpret_cast<V16*>(a.G + (p * a.n + qq) * CZ + ch + 8 * (lane & 3)) = v;
+          }
+          wave_sync();
+        }
+      }
+    }
+    if (c + 1 < NCHUNK) w_put(stg, sW[(c + 1) & 1], tid);
+    __syncthreads();
   }
 }
 
-// pre [P][640] -> A, B [128][Np][Np] (gated, channel-major, zero outside the
-// N x N pairs) and G = s(g_pre) [P][128].  One block per (row p < Np, 64
-// consecutive q < Np); the channel-major rows go through an LDS transpose.
-// The pair-major side is read 16 threads per pair, 8 channels each (whole
-// 256-byte blocks of a pair's row per instruction).
+// Input side backward, fused: recompute the a and b projections from the
+// saved xhat (the forward's operands, so the same products), take the gate
+// derivative with dA / dB (channel-major) into dpre = (d a_p, d a_g, d b_p,
+// d b_g) and, with d g_pre (written by the output side's backward),
+// dX = dpre . W.  One wave per 32 pairs (p, q0 .. q0 + 31), four waves per
+// block; the weight chunks are the forward's.  For each chunk the wave's dA
+// rows come in through a per-wave tile, the two 32-row halves of dpre go out
+// through two more: the transposing LDS read gives each lane (pair) 8
+// consecutive channels, which are both the dX MFMA operand and a pair-major
+// store of dpre (for the weight-gradient GEMM).  The dX operand of the weights
+// is the transposing read of the same chunk (lane = input channel).  dX is
+// written in fp32 for the LayerNorm backward.
+__global__ __launch_bounds__(256, 2) void front_bwd_kernel(TmArgs a, const bf16* __restrict__ w) {
+  __shared__ __align__(16) bf16 sW[2][4 * WSUB];
+  __shared__ __align__(16) bf16 sD[4][2][32 * PITCH];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const long long p = blockIdx.y;
+  const long long q0 = (long long)blockIdx.x * 128 + 32 * wv;
+  const long long q = q0 + l32;
+  const bool live = p < a.n && q < a.n;
+  const long long pp = live ? p * a.n + q : 0;
+  WStage stg;
+  w_fetch(stg, w, 0, tid);
+  Op<bf16> X[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; kk++) X[kk] = live ? load_c_op(a.xhat + pp * CZ + 32 * kk, g) : zero_op<bf16>();
+  w_put(stg, sW[0], tid);
+  __syncthreads();
+  const long long np2 = (long long)a.np * a.np;
+  f32x16 dx[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) dx[i] = zero16();
+  bf16* const t0 = sD[wv][0];
+  bf16* const t1 = sD[wv][1];
+  for (int c = 0; c < NCHUNK; c++) {
+    if (c + 1 < NCHUNK) w_fetch(stg, w, c + 1, tid);
+    const bf16* wb = sW[c & 1];
+    Op<bf16> dpo, dgo;      // dpre of the chunk's two row halves; lane = pair, element = row 16 u + 8 g + e
+    if (c < 8) {
+      const int blk = c >> 2, cb = c & 3;
+      // dA / dB rows 32 cb .. 32 cb + 31 at the wave's 32 pairs, through t0
+      const bf16* dsrc = (blk ? a.dB : a.dA) + (long long)(32 * cb) * np2 + p * a.np + q0;
+#pragma unroll
+      for (int it = 0; it < 2; it++)
+        *reinterpret_cast<V16*>(t0 + ((lane >> 2) + 16 * it) * PITCH + 8 * (lane & 3)) =
+            *reinterpret_cast<const V16*>(dsrc + ((lane >> 2) + 16 * it) * np2 + 8 * (lane & 3));
+      f32x16 ap = zero16(), ag = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; kk++) {
+        ap = mma32(X[kk], lds_c_op(wb + kk * WSUB + l32 * PITCH, g), ap);
+        ag = mma32(X[kk], lds_c_op(wb + kk * WSUB + (32 + l32) * PITCH, g), ag);
+      }
+      wave_sync();
+      // ap[r]: pair q0 + mrow(g, r), channel 32 cb + l32
+      bf16x4 d4[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) d4[s4] = *reinterpret_cast<const bf16x4*>(t0 + l32 * PITCH + 8 * s4 + 4 * g);
+      wave_sync();
+#pragma unroll
+      for (int s4 = 0; s4 < 4; s4++) {
+        bf16x4 op, og;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const float d = (float)d4[s4][t], sgv = sig(ag[4 * s4 + t]);
+          op[t] = (bf16)(d * sgv);
+          og[t] = (bf16)(d * ap[4 * s4 + t] * sgv * (1.0f - sgv));
+        }
+        tile_put4(t0, l32, g, s4, op);
+        tile_put4(t1, l32, g, s4, og);
+      }
+      wave_sync();
+      dpo = lds_tr_op<MAP_C>(t0, PITCH, lane);
+      dgo = lds_tr_op<MAP_C>(t1, PITCH, lane);
+      if (live) {
+        store_c_op(a.dpre + pp * PRE + WCH * c, dpo, g);
+        store_c_op(a.dpre + pp * PRE + WCH * c + 32, dgo, g);
+      }
+      wave_sync();
+    } else {
+      // the g block: d g_pre is already pair-major in dpre (its chunk-order columns are the natural ones)
+      dpo = load_c_op(a.dpre + pp * PRE + WCH * c, g);
+      dgo = load_c_op(a.dpre + pp * PRE + WCH * c + 32, g);
+    }
+#pragma unroll
+    for (int cib = 0; cib < 4; cib++) {
+      // lane = input channel 32 cib + l32, element = chunk row (16 u + 8 g + e) of each half
+      dx[cib] = mma32(lds_tr_op<MAP_C>(wb + cib * WSUB, PITCH, lane), dpo, dx[cib]);
+      dx[cib] = mma32(lds_tr_op<MAP_C>(wb + cib * WSUB + 32 * PITCH, PITCH, lane), dgo, dx[cib]);
+    }
+    if (c + 1 < NCHUNK) w_put(stg, sW[(c + 1) & 1], tid);
+    __syncthreads();
+  }
+  // dx[cib][r]: input channel 32 cib + mrow(g, r), pair q0 + l32
+  if (!live) return;
+#pragma unroll
+  for (int cib = 0; cib < 4; cib++)
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++)
+      *reinterpret_cast<f32x4*>(a.dX + pp * CZ + 32 * cib + 8 * s4 + 4 * g) =
+          (f32x4){dx[cib][4 * s4], dx[cib][4 * s4 + 1], dx[cib][4 * s4 + 2], dx[cib][4 * s4 + 3]};
+}
+
+// Output-side per-pair kernels: one block per (row p, 64 consecutive q).
 constexpr int TQ = 64;          // pairs per block along q
 constexpr int TP = TQ + 8;      // LDS pitch of a padded [channel][q] tile (bf16 elements)
-// Swizzled unpadded [channel][q] tile (128 x 64 bf16): element (c, q) at
-// c * 64 + 8 ((q / 8) ^ (c / 8) mod 8) + q % 8.  16-byte row pieces stay whole,
-// and the 2-byte column accesses of 16 channel rows at one q spread over the
-// banks (at most two rows share one).
-__device__ __forceinline__ int tq_off(int c, int q) { return c * TQ + ((((q >> 3) ^ (c >> 3)) & 7) << 3) + (q & 7); }
-__device__ __forceinline__ int tq_piece(int c, int k) { return c * TQ + (((k ^ (c >> 3)) & 7) << 3); }
-
-__global__ __launch_bounds__(256) void gate_in_kernel(TmArgs a) {
-  __shared__ __align__(16) bf16 sT[CH * TQ];
-  const int tid = threadIdx.x, slot = tid >> 4, c0 = (tid & 15) * 8;
-  const long long p = blockIdx.y, q0 = (long long)blockIdx.x * TQ;
-  const long long np2 = (long long)a.np * a.np;
-  for (int which = 0; which < 2; which++) {     // 0: a from (a_p, a_g), 1: b from (b_p, b_g)
-#pragma unroll
-    for (int it = 0; it < TQ / 16; it++) {
-      const int qi = it * 16 + slot;
-      const long long q = q0 + qi;
-      const bool live = p < a.n && q < a.n;
-      const bf16* pre = a.pre + (live ? p * a.n + q : 0) * PRE + which * 2 * CH;
-      float vp[8], vg[8];
-      load8f(pre + c0, vp);
-      load8f(pre + CH + c0, vg);
-#pragma unroll
-      for (int i = 0; i < 8; i++) sT[tq_off(c0 + i, qi)] = (bf16)(live ? sig(vg[i]) * vp[i] : 0.0f);
-    }
-    __syncthreads();
-    bf16* dst = (which ? a.B : a.A) + p * a.np + q0;
-#pragma unroll
-    for (int r = 0; r < 4; r++) {               // 128 channel rows x 8 pieces of 16 bytes
-      const int idx = tid + 256 * r, c = idx >> 3, k = idx & 7;
-      *reinterpret_cast<V16*>(dst + c * np2 + 8 * k) = *reinterpret_cast<const V16*>(sT + tq_piece(c, k));
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int it = 0; it < TQ / 16; it++) {
-    const long long q = q0 + it * 16 + slot;
-    if (p >= a.n || q >= a.n) continue;
-    const long long pp = p * a.n + q;
-    float vg[8];
-    load8f(a.pre + pp * PRE + 4 * CH + c0, vg);
-#pragma unroll
-    for (int i = 0; i < 8; i++) vg[i] = sig(vg[i]);
-    store8(a.G + pp * CZ + c0, vg);
-  }
-}
 
 // T [128][Np][Np] -> tl = LN(T) [P][128] and statistics.  One block per (p < N,
 // 64 consecutive q < N); 4 threads per pair, 32 channels each.
@@ -453,46 +666,6 @@ __global__ __launch_bounds__(256) void ln_out_bwd_kernel(TmArgs a) {
   }
 }
 
-// Gate backward of the input side: dA, dB [128][Np][Np], pre [P][640] ->
-// dpre[:, 0 .. 511] = (d a_p, d a_g, d b_p, d b_g).  One block per (p < N, 64
-// q); the pair-major side 16 threads per pair, 8 channels each.
-__global__ __launch_bounds__(256) void gate_in_bwd_kernel(TmArgs a) {
-  __shared__ __align__(16) bf16 sT[CH * TQ];
-  const int tid = threadIdx.x, slot = tid >> 4, c0 = (tid & 15) * 8;
-  const long long p = blockIdx.y, q0 = (long long)blockIdx.x * TQ;
-  const long long np2 = (long long)a.np * a.np;
-  for (int which = 0; which < 2; which++) {
-    const bf16* src = (which ? a.dB : a.dA) + p * a.np + q0;
-#pragma unroll
-    for (int r = 0; r < 4; r++) {
-      const int idx = tid + 256 * r, c = idx >> 3, k = idx & 7;
-      *reinterpret_cast<V16*>(sT + tq_piece(c, k)) = *reinterpret_cast<const V16*>(src + c * np2 + 8 * k);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < TQ / 16; it++) {
-      const int qi = it * 16 + slot;
-      const long long q = q0 + qi;
-      if (q >= a.n) continue;
-      const long long pp = p * a.n + q;
-      const bf16* pre = a.pre + pp * PRE + which * 2 * CH;
-      bf16* dpre = a.dpre + pp * PRE + which * 2 * CH;
-      float vp[8], vg[8], dp[8], dg[8];
-      load8f(pre + c0, vp);
-      load8f(pre + CH + c0, vg);
-#pragma unroll
-      for (int i = 0; i < 8; i++) {
-        const float d = (float)sT[tq_off(c0 + i, qi)], sgv = sig(vg[i]);
-        dp[i] = d * sgv;
-        dg[i] = d * vp[i] * sgv * (1.0f - sgv);
-      }
-      store8(dpre + c0, dp);
-      store8(dpre + CH + c0, dg);
-    }
-    __syncthreads();
-  }
-}
-
 // LayerNorm backward of the input norm: dX [P][128] (fp32), z and the
 // statistics -> dz (caller frame), and per-block partials of dgamma_in /
 // dbeta_in ([block][2][128]).  A block takes LNB_PAIRS consecutive pairs, 16
@@ -549,25 +722,49 @@ __global__ __launch_bounds__(256) void ln_in_bwd_kernel(TmArgs a) {
   a.part_ln_in[((long long)blockIdx.x * 2 + which) * CZ + c] = s;
 }
 
-// sum_s part[s][e] (s ascending, fp32), rounded once to bf16.  Weight
-// gradients (out2 == NULL): rows of 128 elements in blocks of 128 rows; row
-// block rb of the partials goes to row block perm[rb] of `out` (the caller's
-// order of the weight blocks).  LayerNorm parameters (out2 != NULL, 256
-// elements): e < 128 to out[e] (gamma), the rest to out2[e - 128] (beta).
+// sum_s part[s][e] (s ascending, fp32), rounded once to bf16, for the weight
+// gradients: rows of 128 elements.  chunked = 0: rows in the caller's order
+// (dW_o); chunked = 1: partial row R (chunk order, from dpre) goes to caller
+// row chunk_src_row(R) (dW_in).
+// Row R of the chunk-ordered kernel-frame input weights (see the fused input
+// side) is row chunk_src_row(R) of the caller's w_in: its kernel-frame row,
+// whose 128-row block is then taken from block src[...] of the caller (the
+// incoming edges exchange the a and b blocks).
+__device__ __forceinline__ int chunk_src_row(int R, const int (&src)[5]) {
+  const int c = R >> 6, r = R & 63;
+  const int kr = c < 8 ? 256 * (c >> 2) + 32 * (c & 3) + (r < 32 ? r : CH + r - 32) : R;
+  return src[kr >> 7] * 128 + (kr & 127);
+}
+
 __global__ __launch_bounds__(256) void sum_kernel(const float* part, int nparts, long long per_part, bf16* out,
-                                                  int4 perm_lo, int perm4, bf16* out2) {
+                                                  int4 src_lo, int src4, int chunked) {
   const long long e = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= per_part) return;
   float s = 0.0f;
   for (int i = 0; i < nparts; i++) s += part[(long long)i * per_part + e];
-  if (out2 != nullptr) {
-    (e < 128 ? out : out2)[e & 127] = (bf16)s;
-    return;
+  const int row = (int)(e / 128), col = (int)(e % 128);
+  const int src[5] = {src_lo.x, src_lo.y, src_lo.z, src_lo.w, src4};
+  out[(long long)(chunked ? chunk_src_row(row, src) : row) * 128 + col] = (bf16)s;
+}
+
+// LayerNorm parameter gradients: part [nparts][256] (gamma in elements 0 ..
+// 127, beta in 128 .. 255).  One block per element: thread t adds the parts
+// t, t + 256, t + 512, ... in that order, then a fixed pairwise tree over the
+// 256 threads; rounded once to bf16.
+__global__ __launch_bounds__(256) void ln_param_sum_kernel(const float* part, int nparts, bf16* gamma, bf16* beta) {
+  __shared__ float sAcc[256];
+  const int e = blockIdx.x, t = threadIdx.x;
+  float s = 0.0f;
+#pragma unroll 4
+  for (int i = t; i < nparts; i += 256) s += part[(long long)i * 256 + e];
+  sAcc[t] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) sAcc[t] += sAcc[t + w];
+    __syncthreads();
   }
-  const long long row = e / 128, col = e % 128;
-  const int rb = (int)(row / 128);
-  const int perm[5] = {perm_lo.x, perm_lo.y, perm_lo.z, perm_lo.w, perm4};
-  out[((long long)perm[rb] * 128 + row % 128) * 128 + col] = (bf16)s;
+  if (t == 0) (e < 128 ? gamma : beta)[e & 127] = (bf16)sAcc[0];
 }
 
 // First level of a fixed-order sum over many partials: out[g][e] = sum of
@@ -584,14 +781,14 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float* part, int n
   out[(long long)g * per_part + e] = s;
 }
 
-// kernel-frame input weights: blocks of 128 rows copied in the order `src_block`
+// wk [640][128]: the input weights in chunk order
 __global__ __launch_bounds__(256) void permute_w_kernel(const bf16* w, bf16* out, int4 src_lo, int src4) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;  // one 16-byte piece: 640 rows x 16 pieces
   if (t >= PRE * 16) return;
-  const int row = t >> 4, piece = t & 15, blk = row >> 7;
+  const int row = t >> 4, piece = t & 15;
   const int src[5] = {src_lo.x, src_lo.y, src_lo.z, src_lo.w, src4};
   *reinterpret_cast<V16*>(out + row * CZ + piece * 8) =
-      *reinterpret_cast<const V16*>(w + (src[blk] * 128 + (row & 127)) * CZ + piece * 8);
+      *reinterpret_cast<const V16*>(w + chunk_src_row(row, src) * CZ + piece * 8);
 }
 
 }  // namespace tm
@@ -608,9 +805,9 @@ size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   long long P, np;
   // saved (forward -> backward)
-  size_t xhat, mean_in, rstd_in, pre, A, B, G, T, mean_out, rstd_out, tl, u, w_perm, saved_total;
+  size_t xhat, mean_in, rstd_in, A, B, G, T, mean_out, rstd_out, tl, u, w_perm, saved_total;
   // backward workspace
-  size_t du, dpre, dtl, dT, dA, dB, dX, part_wo, part_win, grp_wo, grp_win, part_lo, part_li, grp_lo, grp_li, ws_total;
+  size_t du, dpre, dtl, dT, dA, dB, dX, part_wo, part_win, grp_wo, grp_win, part_lo, part_li, ws_total;
   int ksplit_o, ksplit_i;
   long long kchunk_o, kchunk_i, lo_blocks, li_blocks;
 };
@@ -626,7 +823,6 @@ Layout layout(int n) {
   L.xhat = take(P * CZ * 2);
   L.mean_in = take(P * 4);
   L.rstd_in = take(P * 4);
-  L.pre = take(P * PRE * 2);
   L.A = take(np2 * CH * 2);
   L.B = take(np2 * CH * 2);
   L.G = take(P * CZ * 2);
@@ -659,8 +855,6 @@ Layout layout(int n) {
   L.grp_win = take((size_t)((L.ksplit_i + GROUP - 1) / GROUP) * PRE * CZ * 4);
   L.part_lo = take((size_t)L.lo_blocks * 2 * CH * 4);
   L.part_li = take((size_t)L.li_blocks * 2 * CZ * 4);
-  L.grp_lo = take((size_t)((L.lo_blocks + GROUP - 1) / GROUP) * 2 * CH * 4);
-  L.grp_li = take((size_t)((L.li_blocks + GROUP - 1) / GROUP) * 2 * CZ * 4);
   L.ws_total = o;
   return L;
 }
@@ -675,7 +869,6 @@ TmArgs base_args(int n, int incoming, const Layout& L, char* saved) {
   a.xhat = (bf16*)(saved + L.xhat);
   a.mean_in = (float*)(saved + L.mean_in);
   a.rstd_in = (float*)(saved + L.rstd_in);
-  a.pre = (bf16*)(saved + L.pre);
   a.A = (bf16*)(saved + L.A);
   a.B = (bf16*)(saved + L.B);
   a.G = (bf16*)(saved + L.G);
@@ -720,11 +913,9 @@ hipError_t trimul_fwd(int n, int incoming, const TmParams& w, const bf16* z, bf1
   if ((e = mark(0)) != hipSuccess) return e;
   hipLaunchKernelGGL(permute_w_kernel, dim3(blocks_for(PRE * 16)), dim3(256), 0, st, w.w_in, wk, blocks_lo(incoming), 4);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(ln_in_kernel, dim3(blocks_for(L.P * 16)), dim3(256), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  // pre = xhat . W^T
-  if ((e = gemm<0, 0, false>(gemm_args((int)L.P, PRE, CZ, a.xhat, CZ, wk, CZ, a.pre, PRE), st)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gate_in_kernel, dim3((unsigned)(L.np / TQ), (unsigned)L.np), dim3(256), 0, st, a);
+  // LayerNorm, projections and gates: A, B (channel-major), G, xhat
+  // two rows of pairs per wave: each weight operand read from LDS feeds two products
+  hipLaunchKernelGGL(front_fwd_kernel<2>, dim3((unsigned)(L.np / 128), (unsigned)(L.np / 2)), dim3(256), 0, st, a, wk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // T_c = A_c B_c^T for every channel
   GemmArgs c = gemm_args((int)L.np, (int)L.np, (int)L.np, a.A, L.np, a.B, L.np, a.T, L.np);
@@ -786,10 +977,10 @@ hipError_t trimul_bwd(int n, int incoming, const TmParams& w, const bf16* z, con
   gb.X = a.dT; gb.Y = a.A; gb.D = a.dB;
   if ((e = gemm<1, 1, false>(gb, st)) != hipSuccess) return e;
   if ((e = mark(3)) != hipSuccess) return e;
-  hipLaunchKernelGGL(gate_in_bwd_kernel, dim3((unsigned)((n + TQ - 1) / TQ), (unsigned)n), dim3(256), 0, st, a);
+  // gate derivatives -> dpre (pair-major) and dX = dpre . W (fp32)
+  hipLaunchKernelGGL(front_bwd_kernel, dim3((unsigned)(L.np / 128), (unsigned)n), dim3(256), 0, st, a, wk);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // dX = dpre . W (fp32), dW partials = dpre^T xhat
-  if ((e = gemm<0, 1, true>(gemm_args((int)L.P, CZ, PRE, a.dpre, PRE, wk, CZ, a.dX, CZ), st)) != hipSuccess) return e;
+  // dW_in partials = dpre^T xhat
   GemmArgs gi = gemm_args(PRE, CZ, (int)L.P, a.dpre, PRE, a.xhat, CZ, part_win, CZ);
   gi.ksplit = L.ksplit_i; gi.kchunk = L.kchunk_i; gi.d_split = (long long)PRE * CZ;
   if ((e = gemm<1, 1, true>(gi, st)) != hipSuccess) return e;
@@ -804,27 +995,20 @@ hipError_t trimul_bwd(int n, int incoming, const TmParams& w, const bf16* z, con
                      (long long)CZ * CH, grp_wo);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sum_kernel, dim3(blocks_for(CZ * CH)), dim3(256), 0, st, grp_wo, gwo, (long long)CZ * CH,
-                     d.dw_out, id, 4, (bf16*)nullptr);
+                     d.dw_out, id, 4, 0);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(group_sum_kernel, dim3(blocks_for(PRE * CZ), gwi), dim3(256), 0, st, part_win, L.ksplit_i,
                      (long long)PRE * CZ, grp_win);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(sum_kernel, dim3(blocks_for(PRE * CZ)), dim3(256), 0, st, grp_win, gwi, (long long)PRE * CZ,
-                     d.dw_in, blocks_lo(incoming), 4, (bf16*)nullptr);
+                     d.dw_in, blocks_lo(incoming), 4, 1);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // LayerNorm parameters: [block][2][128] partials, blocks in order (groups of 64, then the groups)
-  const int glo = (int)((L.lo_blocks + GROUP - 1) / GROUP), gli = (int)((L.li_blocks + GROUP - 1) / GROUP);
-  float* grp_lo = (float*)(ws + L.grp_lo);
-  float* grp_li = (float*)(ws + L.grp_li);
-  hipLaunchKernelGGL(group_sum_kernel, dim3(1, glo), dim3(256), 0, st, a.part_ln_out, (int)L.lo_blocks, 2ll * CH,
-                     grp_lo);
+  // LayerNorm parameters: [block][2][128] partials
+  hipLaunchKernelGGL(ln_param_sum_kernel, dim3(2 * CH), dim3(256), 0, st, a.part_ln_out, (int)L.lo_blocks,
+                     d.dgamma_out, d.dbeta_out);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, st, grp_lo, glo, 2ll * CH, d.dgamma_out, id, 4, d.dbeta_out);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(group_sum_kernel, dim3(1, gli), dim3(256), 0, st, a.part_ln_in, (int)L.li_blocks, 2ll * CZ,
-                     grp_li);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(sum_kernel, dim3(1), dim3(256), 0, st, grp_li, gli, 2ll * CZ, d.dgamma_in, id, 4, d.dbeta_in);
+  hipLaunchKernelGGL(ln_param_sum_kernel, dim3(2 * CZ), dim3(256), 0, st, a.part_ln_in, (int)L.li_blocks,
+                     d.dgamma_in, d.dbeta_in);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return mark(4);
 }

@@ -28,7 +28,7 @@ struct TmArgs {
   float eps;
   const bf16 *z, *dy, *gamma_in, *beta_in, *gamma_out, *beta_out;
   bf16 *y, *dz;
-  bf16 *xhat, *pre, *A, *B, *G, *T, *tl, *u;             // kept from the forward for the backward
+  bf16 *xhat, *A, *B, *G, *T, *tl, *u;             // kept from the forward for the backward
   float *mean_in, *rstd_in, *mean_out, *rstd_out;
   bf16 *du, *dpre, *dT, *dA, *dB;                        // backward workspace
   float *dtl, *dX, *part_ln_out, *part_ln_in;
