@@ -208,8 +208,9 @@ def time_block(lib, hip, dev, stream, n, steps, warmup, no_end):
 
 
 def time_chunked(lib, hip, dev, stream, n, steps, warmup, rows_list=(768, 128, 32)):
-    """Chunked inference of the starting-node block (tri_attn_block_fwd_chunked) at several chunk sizes:
-    forward time per call and the workspace it needs, next to the unchunked forward's intermediates."""
+    """Chunked inference of the starting-node block at several chunk sizes: tri_attn_block_fwd_chunked
+    (front end, attention, output linear) and tri_attn_block_fwd_fused (q and the gate projected inside the
+    attention kernel, no saved attention), forward time per call and the workspace each needs."""
     import torch
 
     import triangle_attention_tri_amd as ta
@@ -221,26 +222,31 @@ def time_chunked(lib, hip, dev, stream, n, steps, warmup, rows_list=(768, 128, 3
     res = []
     for rows in rows_list:
         rows = min(rows, n)
-        need = lib.tri_attn_block_fwd_chunked_workspace_size(n, cz, H, c, ta.BF16, rows)
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        entry = {"rows_per_chunk": rows}
+        for kind, size_fn, fn in (("chunked", lib.tri_attn_block_fwd_chunked_workspace_size,
+                                   lib.tri_attn_block_fwd_chunked),
+                                  ("fused", lib.tri_attn_block_fwd_fused_workspace_size, lib.tri_attn_block_fwd_fused)):
+            need = size_fn(n, cz, H, c, ta.BF16, rows)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
 
-        def call():
-            st = lib.tri_attn_block_fwd_chunked(n, cz, H, c, ta.BF16, rows, P(x["z"]), P(x["gamma"]), P(x["beta"]),
-                                                ctypes.c_float(1e-5), P(x["w_qkvg"]), P(x["w_bias"]), P(x["w_o"]),
-                                                None, P(y), P(ws), ctypes.c_size_t(need), stream)
-            assert st == 0, st
-        for _ in range(warmup):
-            call()
-        t0, t1 = hip.event(), hip.event()
-        torch.cuda.synchronize()
-        hip.record(t0, stream)
-        for _ in range(steps):
-            call()
-        hip.record(t1, stream)
-        torch.cuda.synchronize()
-        res.append({"rows_per_chunk": rows, "ms": round(hip.ms(t0, t1) / steps, 4),
-                    "workspace_mib": round(need / 2 ** 20, 1)})
-        del ws
+            def call():
+                st = fn(n, cz, H, c, ta.BF16, rows, P(x["z"]), P(x["gamma"]), P(x["beta"]), ctypes.c_float(1e-5),
+                        P(x["w_qkvg"]), P(x["w_bias"]), P(x["w_o"]), None, P(y), P(ws), ctypes.c_size_t(need), stream)
+                assert st == 0, (kind, st)
+            for _ in range(warmup):
+                call()
+            t0, t1 = hip.event(), hip.event()
+            torch.cuda.synchronize()
+            hip.record(t0, stream)
+            for _ in range(steps):
+                call()
+            hip.record(t1, stream)
+            torch.cuda.synchronize()
+            pre = "" if kind == "chunked" else "fused_"
+            entry[pre + "ms"] = round(hip.ms(t0, t1) / steps, 4)
+            entry[pre + "workspace_mib"] = round(need / 2 ** 20, 1)
+            del ws
+        res.append(entry)
     return res
 
 
@@ -594,7 +600,7 @@ def main():
     torch.cuda.empty_cache()
 
     block = None if args.no_block else time_block(lib, hip, dev, stream, n, max(3, args.steps // 2), 2, args.no_end)
-    chunked = None if args.no_chunked else time_chunked(lib, hip, dev, stream, n, 3, 1)
+    chunked = None if args.no_chunked else time_chunked(lib, hip, dev, stream, n, 5, 2)
     configs = None if args.no_configs else time_configs(lib, hip, dev, stream, sorted(CONFIGS),
                                                         max(5, args.steps // 2), 3)
     trimul = None if args.no_trimul else time_trimul(lib, hip, dev, stream, n, max(3, args.steps // 4), 2)

@@ -341,6 +341,39 @@ int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_
                                const uint8_t *mask, void *y,
                                void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Fused inference forward of the starting-node block.  The pages advocate
+ * folding the front end (LayerNorm and the q / k / v / gate projections) into
+ * the attention kernel (HelixFold review, "提出的方法": fused gated
+ * self-attention; MegaFold explainer, EvoFusion paragraph).  This runs the
+ * chunked forward's two passes with pass 2's front end split:
+ *
+ *   pass 1, each chunk: LayerNorm + pair-bias projection (as the chunked forward);
+ *   pass 2, each chunk: LayerNorm + k / v projections only; then the attention
+ *   kernel computes, in its prologue, LayerNorm and the q and gate projections
+ *   of its own 32 queries per wave in registers (q and the gate never reach
+ *   memory), runs the attention, applies the gate, and writes only the gated
+ *   output (no saved attention, no log-sum-exp: there is no backward); output
+ *   linear into the chunk's rows of y.
+ *
+ * y is bit for bit the y of tri_attn_block_fwd_chunked (and of the unchunked
+ * block) for every rows_per_chunk: the fused prologue repeats the front end's
+ * expressions and products.  Sizes, dtypes, layouts and errors as for
+ * tri_attn_block_fwd_chunked.
+ * ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace (0 on bad args): the full bias, one chunk's k, v,
+ * gated output and LayerNorm statistics, and the attention forward's workspace. */
+size_t tri_attn_block_fwd_fused_workspace_size(int n, int cz, int h, int c, int dtype, int rows_per_chunk);
+
+/* The fused forward: writes y.  workspace: 256-byte aligned, at least
+ * tri_attn_block_fwd_fused_workspace_size bytes, contents on entry ignored. */
+int tri_attn_block_fwd_fused(int n, int cz, int h, int c, int dtype, int rows_per_chunk,
+                             const void *z, const void *ln_gamma, const void *ln_beta, float ln_eps,
+                             const void *w_qkvg, const void *w_bias, const void *w_o,
+                             const uint8_t *mask, void *y,
+                             void *workspace, size_t workspace_bytes, tri_attn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

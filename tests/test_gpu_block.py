@@ -165,6 +165,40 @@ def test_block_fwd_chunked(device):
     assert r >= 37 and need <= sizes[37] + 100 and torch.equal(y, y_full)
 
 
+@pytest.mark.parametrize("n,masked", [(96, True), (130, False), (37, True)])
+def test_block_fwd_fused(device, n, masked):
+    """Fused inference of the starting-node block (LayerNorm, q and the gate projected inside the attention
+    kernel): y is bit for bit the chunked forward's for whole, uneven and single-row chunks (ragged n and a fully
+    masked row included), and matches the block oracle."""
+    x = inputs.block_inputs(n, seed=61 + n, affine=True)
+    if masked:
+        x["mask"] = inputs.random_mask(n, seed=62 + n, p_keep=0.8, full_rows=(3,))
+    xd = dev(x, device)
+    w = (xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"])
+    mask = xd.get("mask")
+    y_ref, _, _ = ta.block_fwd_chunked(*w, mask=mask, rows_per_chunk=n)
+    torch.cuda.synchronize()
+    ref = B.block_fwd(x["z"], x["gamma"], x["beta"], x["w_qkvg"], x["w_bias"], x["w_o"], H, C, mask=x.get("mask"))
+    for rows in (n, 32, 1):
+        y, need = ta.block_fwd_fused(*w, mask=mask, rows_per_chunk=rows)
+        torch.cuda.synchronize()
+        e = assert_close(f"y(fused, rows {rows})", y.cpu(), ref["y"], TOL)
+        assert torch.equal(y, y_ref), f"n={n} rows_per_chunk={rows}: fused y differs from the chunked forward"
+        log(f"fused block n={n} rows={rows}: error {e:.2e}, workspace {need / 2**20:.2f} MiB, bitwise equal")
+
+
+@pytest.mark.parametrize("n", [768])
+def test_block_fwd_fused_n768(device, n):
+    """The fused inference block at the benchmark's size, bitwise against the chunked forward."""
+    x = inputs.block_inputs(n, seed=68, affine=True)
+    xd = dev(x, device)
+    w = (xd["z"], xd["gamma"], xd["beta"], xd["w_qkvg"], xd["w_bias"], xd["w_o"])
+    y_ref, _, _ = ta.block_fwd_chunked(*w, rows_per_chunk=n)
+    y, _ = ta.block_fwd_fused(*w)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+
+
 def test_out_proj_n768(device):
     """Output linear forward and backward at the block's full size (768 x 768 = 589,824 pairs): the persistent
     multi-tile loop, the cross-tile prefetch and the per-workgroup weight-gradient partials all run here."""

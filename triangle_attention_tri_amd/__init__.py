@@ -24,6 +24,7 @@ import os
 __all__ = ["fwd", "bwd", "workspace_size", "bwd_chunk_rows", "fwd_workspace_size", "max_n", "TriAttnFunction",
            "tri_attn", "lib_path",
            "load", "ln_proj_fwd", "ln_proj_bwd", "out_proj_fwd", "out_proj_bwd", "block_fwd", "block_bwd",
+           "block_fwd_chunked", "block_fwd_fused",
            "trimul_fwd", "trimul_bwd"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -85,6 +86,10 @@ def load():
     lib.tri_attn_block_chunk_rows.restype = i
     lib.tri_attn_block_fwd_chunked.argtypes = [i] * 6 + [vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.tri_attn_block_fwd_chunked.restype = i
+    lib.tri_attn_block_fwd_fused_workspace_size.argtypes = [i] * 6
+    lib.tri_attn_block_fwd_fused_workspace_size.restype = sz
+    lib.tri_attn_block_fwd_fused.argtypes = [i] * 6 + [vp, vp, vp, f, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.tri_attn_block_fwd_fused.restype = i
     lib.tri_mul_saved_size.argtypes = [i] * 4
     lib.tri_mul_saved_size.restype = sz
     lib.tri_mul_workspace_size.argtypes = [i] * 4
@@ -426,6 +431,31 @@ def block_fwd_chunked(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_c
                                         _ptr(workspace), ctypes.c_size_t(need), _stream(z.device))
     _check(st, "tri_attn_block_fwd_chunked")
     return y, int(rows_per_chunk), need
+
+
+def block_fwd_fused(z, gamma, beta, w_qkvg, w_bias, w_o, mask=None, rows_per_chunk=None, eps: float = 1e-5,
+                    h: int = 4, c: int = 32, workspace=None):
+    """Fused inference of the starting-node block (tri_attn_block_fwd_fused): LayerNorm, q and the gate
+    projected inside the attention kernel.  ``rows_per_chunk`` defaults to n.  Returns (y, workspace_bytes)."""
+    import torch
+    lib = load()
+    n, n2, cz = z.shape
+    if n != n2:
+        raise ValueError("z must be [n, n, c_z]")
+    _prep(dict(z=z, gamma=gamma, beta=beta, w_qkvg=w_qkvg, w_bias=w_bias, w_o=w_o), torch.bfloat16, z.device)
+    _check_mask(mask, z.device, n, n)
+    rows = n if rows_per_chunk is None else int(rows_per_chunk)
+    need = int(lib.tri_attn_block_fwd_fused_workspace_size(n, cz, h, c, BF16, rows))
+    if need == 0:
+        _check(-1, "tri_attn_block_fwd_fused_workspace_size")
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=z.device)
+    y = torch.empty_like(z)
+    st = lib.tri_attn_block_fwd_fused(n, cz, h, c, BF16, rows, _ptr(z), _ptr(gamma), _ptr(beta), ctypes.c_float(eps),
+                                      _ptr(w_qkvg), _ptr(w_bias), _ptr(w_o), _ptr(mask), _ptr(y), _ptr(workspace),
+                                      ctypes.c_size_t(need), _stream(z.device))
+    _check(st, "tri_attn_block_fwd_fused")
+    return y, need
 
 
 # ---------------------------------------------------------------------------

@@ -9,6 +9,7 @@
 
 namespace tri {
 template <typename T, int R> hipError_t launch_fwd(const FwdArgs<T>&, hipStream_t);
+template <int R> hipError_t launch_fwd_fused(const FwdArgs<bf16>&, hipStream_t);
 size_t fwd_workspace_bytes(int n, int h);
 template <typename T, int R> hipError_t launch_bwd(const BwdArgs<T>&, hipStream_t, hipEvent_t*);
 template <typename T, int R> size_t bwd_main_smem(int n);
@@ -208,10 +209,24 @@ WsLayout ws_layout(int n_rows, int n, int h, int dtype) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TRI_ATTN_OK : TRI_ATTN_EHIP; }
 
+// Few rows (a row slice, a small chunk): when the two-row grid of the bf16
+// forward would not fill the device once (3 workgroups per CU), one row per
+// workgroup doubles the workgroups.  Each row's arithmetic is the same in
+// both forms.
+bool fwd_two_rows(const Geo& geo) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
+    const long long blocks2 = (long long)((geo.n + 127) / 128) * ((geo.n_rows + 1) / 2) * geo.H;
+    if (blocks2 < 3ll * cus) return false;
+  }
+  return true;
+}
+
 template <typename T>
 int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const void* bias, const void* gate,
            const uint8_t* mask, void* out, void* attn, int8_t* attn_res, float* lse, void* ws, hipStream_t st) {
-  FwdArgs<T> a;
+  FwdArgs<T> a{};
   a.geo = geo;
   a.q = (const T*)q; a.k = (const T*)k; a.v = (const T*)v;
   a.bias = (const T*)bias; a.gate = (const T*)gate; a.mask = mask;
@@ -219,15 +234,7 @@ int do_fwd(const Geo& geo, const void* q, const void* k, const void* v, const vo
   a.bias_prep = (float*)ws;
   a.attn_res = attn_res;
   if constexpr (sizeof(T) == 2) {
-    // Few rows (a row slice, a small chunk): when the two-row grid would not
-    // fill the device once (3 workgroups per CU), one row per workgroup doubles
-    // the workgroups.  Each row's arithmetic is the same in both forms.
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess) {
-      const long long blocks2 = (long long)((geo.n + 127) / 128) * ((geo.n_rows + 1) / 2) * geo.H;
-      if (blocks2 < 3ll * cus) return hip_status(launch_fwd<T, 1>(a, st));
-    }
+    if (!fwd_two_rows(geo)) return hip_status(launch_fwd<T, 1>(a, st));
   }
   return hip_status(launch_fwd<T, FWD_R>(a, st));
 }
@@ -645,7 +652,7 @@ int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_
     pa.w = (const bf16*)w_qkvg; pa.wb = (const bf16*)w_bias;
     pa.bias = bias + (size_t)r0 * n;
     pa.mean = (float*)mean; pa.rstd = (float*)rstd;
-    if ((st = hip_status(launch_proj_fwd(pa, true, (hipStream_t)stream, true))) != TRI_ATTN_OK) return st;
+    if ((st = hip_status(launch_proj_fwd(pa, true, (hipStream_t)stream, PF_BIAS))) != TRI_ATTN_OK) return st;
   }
   // pass 2: per chunk, projections, attention over the full bias, output linear into y's rows
   for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
@@ -657,6 +664,95 @@ int tri_attn_block_fwd_chunked(int n, int cz, int h, int c, int dtype, int rows_
                       lse, ws + L.fws, L.fws_bytes, stream);
     if (st != TRI_ATTN_OK) return st;
     st = tri_attn_out_proj_fwd(rr * n, h * c, cz, dtype, out, w_o, yb + (size_t)r0 * n * cz, stream);
+    if (st != TRI_ATTN_OK) return st;
+  }
+  return TRI_ATTN_OK;
+}
+
+// Fused inference forward of the block: the chunked forward's structure with
+// the front end of pass 2 split between a k / v-only projection kernel and the
+// attention kernel's own prologue (LayerNorm, q and gate), and no attn / lse.
+static ChunkLayout fused_layout(int n, int h, int c, int R) {
+  ChunkLayout L{};
+  const size_t per_rows = (size_t)R * n * h * c * 2;
+  L.bias = 0;
+  L.k = align256(L.bias + (size_t)h * n * n * 2);
+  L.v = align256(L.k + per_rows);
+  L.out = align256(L.v + per_rows);
+  L.mean = align256(L.out + per_rows);
+  L.rstd = align256(L.mean + (size_t)R * n * 4);
+  L.fws = align256(L.rstd + (size_t)R * n * 4);
+  L.fws_bytes = align256(fwd_workspace_bytes(n, h));
+  L.total = L.fws + L.fws_bytes;
+  return L;
+}
+
+size_t tri_attn_block_fwd_fused_workspace_size(int n, int cz, int h, int c, int dtype, int rows_per_chunk) {
+  if (check_proj(n, n, cz, h, c, dtype) != TRI_ATTN_OK) return 0;
+  if (check_common(n, n, h, c, dtype, 0) != TRI_ATTN_OK) return 0;
+  if (rows_per_chunk < 1 || rows_per_chunk > n) return 0;
+  return fused_layout(n, h, c, rows_per_chunk).total;
+}
+
+int tri_attn_block_fwd_fused(int n, int cz, int h, int c, int dtype, int rows_per_chunk, const void* z,
+                             const void* ln_gamma, const void* ln_beta, float ln_eps, const void* w_qkvg,
+                             const void* w_bias, const void* w_o, const uint8_t* mask, void* y, void* workspace,
+                             size_t workspace_bytes, tri_attn_stream_t stream) {
+  int st = check_proj(n, n, cz, h, c, dtype);
+  if (st != TRI_ATTN_OK) return st;
+  if ((st = check_common(n, n, h, c, dtype, 0)) != TRI_ATTN_OK) return st;
+  if (rows_per_chunk < 1 || rows_per_chunk > n) return TRI_ATTN_EINVAL;
+  if (!(ln_eps > 0.0f) || !(ln_eps < 1.0f)) return TRI_ATTN_EINVAL;
+  const void* a16[] = {z, ln_gamma, ln_beta, w_qkvg, w_bias, w_o, y};
+  for (const void* p : a16)
+    if (!aligned(p, 16)) return TRI_ATTN_EINVAL;
+  const ChunkLayout L = fused_layout(n, h, c, rows_per_chunk);
+  if ((st = check_ws(workspace, workspace_bytes, L.total)) != TRI_ATTN_OK) return st;
+  char* ws = (char*)workspace;
+  bf16* bias = (bf16*)(ws + L.bias);
+  float *mean = (float*)(ws + L.mean), *rstd = (float*)(ws + L.rstd);
+  const bf16* zb = (const bf16*)z;
+  bf16* yb = (bf16*)y;
+  const hipStream_t s = (hipStream_t)stream;
+  auto proj_args = [&](int r0, int rr) {
+    ProjArgs pa{};
+    pa.P = rr * n;
+    pa.n = n;
+    pa.hs = (long long)n * n;
+    pa.eps = ln_eps;
+    pa.x = zb + (size_t)r0 * n * cz;
+    pa.gamma = (const bf16*)ln_gamma; pa.beta = (const bf16*)ln_beta;
+    pa.w = (const bf16*)w_qkvg; pa.wb = (const bf16*)w_bias;
+    pa.mean = mean; pa.rstd = rstd;
+    return pa;
+  };
+  // pass 1: the bias of every pair row (bias-only front end, as in the chunked forward)
+  for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
+    const int rr = min(rows_per_chunk, n - r0);
+    ProjArgs pa = proj_args(r0, rr);
+    pa.bias = bias + (size_t)r0 * n;
+    if ((st = hip_status(launch_proj_fwd(pa, true, s, PF_BIAS))) != TRI_ATTN_OK) return st;
+  }
+  // pass 2: per chunk, k and v, then attention with q and the gate projected in its prologue, output linear
+  for (int r0 = 0; r0 < n; r0 += rows_per_chunk) {
+    const int rr = min(rows_per_chunk, n - r0);
+    ProjArgs pa = proj_args(r0, rr);
+    pa.k = (bf16*)(ws + L.k);
+    pa.v = (bf16*)(ws + L.v);
+    if ((st = hip_status(launch_proj_fwd(pa, true, s, PF_KV))) != TRI_ATTN_OK) return st;
+    FwdArgs<bf16> a{};
+    a.geo = make_geo(rr, n, h, 0);
+    a.k = (const bf16*)(ws + L.k); a.v = (const bf16*)(ws + L.v);
+    a.bias = bias; a.mask = mask ? mask + (size_t)r0 * n : nullptr;
+    a.out = (bf16*)(ws + L.out);
+    a.bias_prep = (float*)(ws + L.fws);
+    a.z = zb + (size_t)r0 * n * cz;
+    a.ln_gamma = (const bf16*)ln_gamma; a.ln_beta = (const bf16*)ln_beta; a.ln_eps = ln_eps;
+    a.w_qkvg = (const bf16*)w_qkvg;
+    // two rows per workgroup unless that grid would not fill the device once (as the plain forward chooses)
+    const bool two = fwd_two_rows(a.geo);
+    if ((st = hip_status(two ? launch_fwd_fused<2>(a, s) : launch_fwd_fused<1>(a, s))) != TRI_ATTN_OK) return st;
+    st = tri_attn_out_proj_fwd(rr * n, h * c, cz, dtype, ws + L.out, w_o, yb + (size_t)r0 * n * cz, stream);
     if (st != TRI_ATTN_OK) return st;
   }
   return TRI_ATTN_OK;

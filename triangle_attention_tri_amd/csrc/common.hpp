@@ -314,6 +314,11 @@ template <typename T> struct FwdArgs {
   float* lse;
   float* bias_prep;  // workspace: bias tiles in per-lane order (bf16 operand tiles; sqrt(c)-scaled fp32 in fp32 runs)
   int8_t* attn_res;  // optional (bf16 runs): rounding-residual codes of attn, [n_rows][H][n][C]; null = not written
+  // fused front end (inference forward of the block): q and the gate are projected inside the kernel from
+  // z [n_rows][n][128] with the LayerNorm parameters and the q / gate rows of w_qkvg [512][128]; attn and
+  // lse are not written
+  const bf16 *z, *ln_gamma, *ln_beta, *w_qkvg;
+  float ln_eps;
 };
 
 constexpr int BWD_TRASH_BYTES = 8192;

@@ -99,11 +99,82 @@ hipError_t launch_bias_op_prep(const Geo& G, const bf16* bias, bf16* out, hipStr
   return hipGetLastError();
 }
 
+// Fused front end of the inference forward: for pair p (lane = the wave's
+// query l32, both lane halves), x = LayerNorm(z_p) in the MFMA operand layout
+// (lane half g holds channels 32 kk + 16 u + 8 g + e) by the same expressions
+// and summation order as the front-end kernel, then q_h and gate_h =
+// x . W^T with the same MFMAs, so both are bit for bit the values the front
+// end would have stored (rounded once to bf16).
+//  * q: the result is D[channel][query] (registers = channels mrow(g, r)).  The
+//    logit MFMA wants the c-map operand (element (u, e) = channel 16 u + 8 g +
+//    e).  mrow(g, 8 u + e) and 16 u + 8 g + e differ by exchanging bits 2 and
+//    3 of the channel, so output row r of the product is taken from weight row
+//    swap23(r): then register 8 u + e holds channel 16 u + 8 g + e and the
+//    rounded accumulator is the operand as it stands.
+//  * gate: D[channel][query] in the layout of the output tile o; kept as 16
+//    bf16 values (register r in element r).
+__device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ void fused_q_gate(const FwdArgs<bf16>& a, long long p, int h, int lane, Op<bf16>& q,
+                                             bf16x8 (&gate)[2]) {
+  constexpr int CZ = 128;
+  const int g = lane >> 5, l32 = lane & 31;
+  Op<bf16> x[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++) x[kb] = load_c_op(a.z + p * CZ + 32 * kb, g);
+  float s = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) s += (float)x[kb].f[u][e];
+  s += __shfl_xor(s, 32);
+  const float mean = s * (1.0f / CZ);
+  float d = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int u = 0; u < 2; u++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float t0 = (float)x[kb].f[u][e] - mean;
+        d += t0 * t0;
+      }
+  d += __shfl_xor(d, 32);
+  const float rstd = 1.0f / sqrtf(d * (1.0f / CZ) + a.ln_eps);
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++)
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const bf16x8 gm = *reinterpret_cast<const bf16x8*>(a.ln_gamma + 32 * kb + 16 * u + 8 * g);
+      const bf16x8 bt = *reinterpret_cast<const bf16x8*>(a.ln_beta + 32 * kb + 16 * u + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        x[kb].f[u][e] = (bf16)(((float)x[kb].f[u][e] - mean) * rstd * (float)gm[e] + (float)bt[e]);
+    }
+  f32x16 aq = zero16(), ag = zero16();
+#pragma unroll
+  for (int kb = 0; kb < 4; kb++) {
+    aq = mma32(load_c_op(a.w_qkvg + (32 * h + swap23(l32)) * CZ + 32 * kb, g), x[kb], aq);
+    ag = mma32(load_c_op(a.w_qkvg + (384 + 32 * h + l32) * CZ + 32 * kb, g), x[kb], ag);
+  }
+  q = acc_op<bf16>(aq);
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) gate[u][e] = (bf16)ag[8 * u + e];
+}
+
 // Longest key axis whose per-tile mask words fit the LDS table below.
 constexpr int FWD_MAX_TILES = 64;
 
-template <typename T, int R>
+// FUSED (bf16, starting node): the block's LayerNorm and its q and gate
+// projections run in the prologue for the wave's 32 queries of each of its R
+// rows (see fused_q_gate); the gate waits in LDS for the epilogue (no
+// registers across the key loop), and attn and lse are not written.
+template <typename T, int R, bool FUSED = false>
 __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void fwd_kernel(FwdArgs<T> a) {
+  static_assert(!FUSED || sizeof(T) == 2, "the fused prologue is bf16");
   constexpr int KP = TILE + kpad<T>();            // LDS row pitch (elements)
   constexpr int EPV = 16 / sizeof(T);             // elements per 16-byte vector
   constexpr int CHUNKS = C / EPV;                 // vectors per 32-element row
@@ -112,6 +183,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void 
   static_assert(NLOAD % 256 == 0, "whole 16-byte pieces per thread");
   __shared__ __align__(16) T sKV[2][2 * R][TILE][KP];  // [buffer][K rows 0..R-1, V rows R..2R-1][key][c]
   __shared__ uint32_t sMask[R][FWD_MAX_TILES];         // kept-key bits of every key tile of the R rows
+  __shared__ __align__(16) bf16 sGate[FUSED ? R * 4 * 64 * 16 : 8];  // fused: [row][wave][lane][16] gate values
 
   const Geo& G = a.geo;
   const int n = G.n;
@@ -153,7 +225,22 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void 
     mb[rr] = NEG_INF;
     l[rr] = 0.0f;
     degen[rr] = rvalid[rr] ? !row_has_valid_key(a.mask, G, row, lane) : false;
-    qop[rr] = (rvalid[rr] && jvalid) ? load_c_op(a.q + row * G.qkv_row + headq + j * G.qkv_pos, g) : zero_op<T>();
+    if constexpr (!FUSED)
+      qop[rr] = (rvalid[rr] && jvalid) ? load_c_op(a.q + row * G.qkv_row + headq + j * G.qkv_pos, g) : zero_op<T>();
+  }
+  // fused front end: q operand and gate of pair (row, j) (lanes past n compute the last pair, never stored)
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int rr = 0; rr < R; rr++) {
+      const int row = min(row0 + rr, G.n_rows - 1), jc = min(j, n - 1);
+      bf16x8 gpk[2];
+      fused_q_gate(a, (long long)row * n + jc, h, lane, qop[rr], gpk);
+      if (!jvalid) qop[rr] = zero_op<T>();
+      bf16x8* gs = reinterpret_cast<bf16x8*>(sGate + ((rr * 4 + w) * 64 + lane) * 16);
+      gs[0] = gpk[0];
+      gs[1] = gpk[1];
+      __builtin_amdgcn_sched_barrier(0);  // one row's LayerNorm and products at a time (registers)
+    }
   }
 
   // K / V staging: every load is unconditional (row and key clamped into range;
@@ -310,7 +397,13 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void 
       float av[4], ov[4];
 #pragma unroll
       for (int t = 0; t < 4; t++) av[t] = o[rr][4 * s4 + t] * inv;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (FUSED) {
+        // gate channels mrow(g, 4 s4 + t) = elements 4 s4 + t of the lane's gate values (its own wave wrote them)
+        const bf16x4 gv = *reinterpret_cast<const bf16x4*>(sGate + ((rr * 4 + w) * 64 + lane) * 16 + 4 * s4);
+#pragma unroll
+        for (int t = 0; t < 4; t++) ov[t] = sigmoidf_((float)gv[t]) * av[t];
+        *reinterpret_cast<bf16x4*>(a.out + ig + c0) = (bf16x4){(bf16)ov[0], (bf16)ov[1], (bf16)ov[2], (bf16)ov[3]};
+      } else if constexpr (sizeof(T) == 2) {
         const bf16x4 gv = *reinterpret_cast<const bf16x4*>(a.gate + ig + c0);
 #pragma unroll
         for (int t = 0; t < 4; t++) ov[t] = sigmoidf_((float)gv[t]) * av[t];
@@ -331,7 +424,7 @@ __global__ __launch_bounds__(256, (sizeof(T) == 2 ? (R == 1 ? 4 : 3) : 2)) void 
         *reinterpret_cast<f32x4*>(a.out + ig + c0) = (f32x4){ov[0], ov[1], ov[2], ov[3]};
       }
     }
-    if (g == 0) {
+    if (!FUSED && g == 0) {
       const float lse = degen[rr] ? MASK_LOGIT + logf((float)n) : (mb[rr] + __log2f(lt)) * LN2;
       a.lse[((long long)row * G.H + h) * n + j] = lse;
     }
@@ -392,6 +485,18 @@ hipError_t launch_fwd(const FwdArgs<T>& a, hipStream_t st) {
   hipLaunchKernelGGL((fwd_kernel<T, R>), dim3(blocks), dim3(256), 0, st, a);
   return hipGetLastError();
 }
+
+template <int R>
+hipError_t launch_fwd_fused(const FwdArgs<bf16>& a, hipStream_t st) {
+  const Geo& G = a.geo;
+  hipError_t e = launch_bias_op_prep(G, a.bias, reinterpret_cast<bf16*>(a.bias_prep), st);
+  if (e != hipSuccess) return e;
+  const int blocks = ((G.n + 127) / 128) * ((G.n_rows + R - 1) / R) * G.H;
+  hipLaunchKernelGGL((fwd_kernel<bf16, R, true>), dim3(blocks), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+template hipError_t launch_fwd_fused<1>(const FwdArgs<bf16>&, hipStream_t);
+template hipError_t launch_fwd_fused<2>(const FwdArgs<bf16>&, hipStream_t);
 
 template hipError_t launch_fwd<bf16, 2>(const FwdArgs<bf16>&, hipStream_t);
 template hipError_t launch_fwd<bf16, 1>(const FwdArgs<bf16>&, hipStream_t);

@@ -111,9 +111,13 @@ __device__ __forceinline__ Op<bf16> w_tr_op(const bf16* sW, int o0, int c0, int 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// BIAS_ONLY (front end): LayerNorm statistics and the pair-bias block only, by
-// the same arithmetic as the full kernel (the chunked inference's first pass).
-template <bool FRONT, bool BIAS_ONLY = false>
+// MODE (front end), always by the same arithmetic as the full kernel:
+//   PF_ALL   every output block;
+//   PF_BIAS  LayerNorm statistics and the pair-bias block only (the chunked
+//            inference's first pass);
+//   PF_KV    k and v only (the fused inference: its first pass writes the
+//            bias, and its attention kernel projects q and the gate itself).
+template <bool FRONT, int MODE = PF_ALL>
 __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   constexpr int M = FRONT ? FRONT_M : 128;
@@ -193,8 +197,11 @@ __global__ __launch_bounds__(PJ_THREADS, 1) void proj_fwd_kernel(ProjArgs a) {
     const int ia = FRONT ? pc / a.n : 0, ib = FRONT ? pc - ia * a.n : 0;
 #pragma unroll
     for (int oc = 0; oc < M / 32; oc++) {
-      if constexpr (BIAS_ONLY) {
+      if constexpr (MODE == PF_BIAS) {
         if (oc != M / 32 - 1) continue;
+      }
+      if constexpr (MODE == PF_KV) {
+        if (oc / PH == 0 || oc / PH >= 3) continue;
       }
       f32x16 acc = zero16();
 #pragma unroll
@@ -549,12 +556,15 @@ size_t proj_workspace_bytes(int P, bool front) {
   return b;
 }
 
-hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st, bool bias_only) {
+hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st, int mode) {
   const int grid = grid_for(a.P);
   hipError_t e;
-  if (front && bias_only) {
-    if ((e = set_smem(proj_fwd_kernel<true, true>, fwd_smem(true))) != hipSuccess) return e;
-    hipLaunchKernelGGL((proj_fwd_kernel<true, true>), dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
+  if (front && mode == PF_BIAS) {
+    if ((e = set_smem(proj_fwd_kernel<true, PF_BIAS>, fwd_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_fwd_kernel<true, PF_BIAS>), dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
+  } else if (front && mode == PF_KV) {
+    if ((e = set_smem(proj_fwd_kernel<true, PF_KV>, fwd_smem(true))) != hipSuccess) return e;
+    hipLaunchKernelGGL((proj_fwd_kernel<true, PF_KV>), dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);
   } else if (front) {
     if ((e = set_smem(proj_fwd_kernel<true>, fwd_smem(true))) != hipSuccess) return e;
     hipLaunchKernelGGL(proj_fwd_kernel<true>, dim3(grid), dim3(PJ_THREADS), fwd_smem(true), st, a);

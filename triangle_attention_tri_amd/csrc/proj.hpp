@@ -22,7 +22,9 @@ struct ProjArgs {
 // Bytes of workspace the backward needs for P pairs (front end or output linear).
 size_t proj_workspace_bytes(int P, bool front);
 // bias_only (front end): only the LayerNorm statistics and the bias block are written.
-hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st, bool bias_only = false);
+// front-end output selection (see proj_fwd_kernel)
+enum { PF_ALL = 0, PF_BIAS = 1, PF_KV = 2 };
+hipError_t launch_proj_fwd(ProjArgs a, bool front, hipStream_t st, int mode = PF_ALL);
 // front: dw0 = dw_qkvg, dw1 = dw_bias, dgamma / dbeta; plain: dw0 = dw_o.
 hipError_t launch_proj_bwd(ProjArgs a, bool front, bf16* dw0, bf16* dw1, bf16* dgamma, bf16* dbeta,
                            hipStream_t st);
