@@ -273,6 +273,21 @@ __device__ __forceinline__ Op<bf16> swz_tr_op_m(const bf16* tile, int lane) {
   }
   return o;
 }
+// MAP_C transposed operand of a swz16 tile (lane <-> column, element (u, e)
+// <-> row 16u + 8g + e): four consecutive rows per transposing read, like the
+// MAP_M form, so it is free of bank conflicts in the same way
+__device__ __forceinline__ Op<bf16> swz_tr_op_c(const bf16* tile, int lane) {
+  const int G = lane >> 4, jp = lane & 15, g = lane >> 5;
+  const int col = 16 * (G & 1) + 4 * (jp & 3);
+  Op<bf16> o;
+#pragma unroll
+  for (int u = 0; u < 2; u++) {
+    const bf16x4 lo = lds_read_tr(tile + swz16(tr_row<MAP_C>(u, 0, g) + (jp >> 2), col));
+    const bf16x4 hi = lds_read_tr(tile + swz16(tr_row<MAP_C>(u, 1, g) + (jp >> 2), col));
+    o.f[u] = (bf16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  return o;
+}
 // Sum of the 16 rounded probabilities a lane holds, from the bf16 operand
 // (v_dot2_f32_bf16 against ones: two products per instruction).
 __device__ __forceinline__ float op_sum(const Op<bf16>& o) {

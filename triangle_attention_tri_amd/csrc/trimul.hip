@@ -53,13 +53,19 @@ namespace tm {
 // (K-major X) and k past the split's end (M- / N-major operands) read as zero;
 // rows past M are not stored.
 constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int PITCH = 40;            // LDS row pitch of a 32 x 32 sub-tile (80 bytes: 16-byte aligned rows)
-constexpr int SUBT = 32 * PITCH;     // elements per sub-tile
+constexpr int PITCH = 40;            // LDS row pitch of the per-wave [32][PITCH] tiles of the per-pair kernels
+constexpr int SUBT = 32 * PITCH;     // elements of one such tile
+// GEMM operand tiles in LDS: four 32 x 32 sub-tiles per operand (32 rows of
+// the 128 each), unpadded and swz16-swizzled (conflict-free row reads,
+// transposing reads and row-piece writes).  Consecutive sub-tiles are 64 bytes
+// apart beyond their 2 KB, so that the M-major staging writes, whose 8-lane
+// passes cover the same row of two sub-tiles, fall on different banks.
+constexpr int GSUB = 32 * 32 + 32;   // elements from one sub-tile to the next
 
 template <int XM, int YM, bool F32OUT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
-  __shared__ __align__(16) bf16 sX[2][4 * SUBT];
-  __shared__ __align__(16) bf16 sY[2][4 * SUBT];
+  __shared__ __align__(16) bf16 sX[2][4 * GSUB];
+  __shared__ __align__(16) bf16 sY[2][4 * GSUB];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;  // the wave's 64 x 64 quarter of the tile
@@ -76,46 +82,51 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
   const bf16* X = a.X + zb * a.x_batch;
   const bf16* Y = a.Y + zb * a.y_batch;
 
-  // staging: two 16-byte pieces of each operand tile per thread
-  V16 px[2], py[2];
+  // staging: two 16-byte pieces of each operand tile per thread, in two
+  // register sets: the loads of K step kt + 2 are issued while step kt is
+  // computed, so each has two steps to land
+  V16 px[2][2], py[2][2];
+  // Loads are unconditional, from clamped addresses, so that no register of a
+  // set is written before its load (the wait for one set never covers the
+  // other): a row past M reads row M - 1 (its products are never stored), and
+  // k past the step's end is zeroed when the pieces are stored to LDS.
   auto load = [&](const bf16* base, long long ld, int mode, long long r0, long long rows, long long k0,
                   V16 (&dst)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const int c = tid + 256 * i;
-      bool ok;
       const bf16* src;
       if (mode == 0) {  // [row][k]: 128 rows of 4 pieces
-        const long long row = r0 + (c >> 2), kk = k0 + (c & 3) * 8;
-        ok = row < rows;
-        src = base + (ok ? row : 0) * ld + kk;
+        const long long row = min(r0 + (c >> 2), rows - 1), kk = min(k0 + (c & 3) * 8, kend - 8);
+        src = base + row * ld + kk;
       } else {          // [k][row]: 32 k-rows of 16 pieces
-        const long long kk = k0 + (c >> 4), row = r0 + (c & 15) * 8;
-        ok = kk < kend;
-        src = base + (ok ? kk : kbeg) * ld + row;
+        const long long kk = min(k0 + (c >> 4), kend - 1), row = r0 + (c & 15) * 8;
+        src = base + kk * ld + row;
       }
-      const V16 v = *reinterpret_cast<const V16*>(src);
-      dst[i] = ok ? v : (V16){0u, 0u, 0u, 0u};
+      dst[i] = *reinterpret_cast<const V16*>(src);
     }
   };
-  auto stash = [&](bf16* tile, int mode, const V16 (&src)[2]) __attribute__((always_inline)) {
+  auto stash = [&](bf16* tile, int mode, const V16 (&src)[2], long long k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2; i++) {
       const int c = tid + 256 * i;
       int off;
-      if (mode == 0) {
+      bool ok;
+      if (mode == 0) {  // sub-tile [row][k]
         const int row = c >> 2, kk = (c & 3) * 8;
-        off = (row >> 5) * SUBT + (row & 31) * PITCH + kk;
-      } else {
+        off = (row >> 5) * GSUB + swz16(row & 31, kk);
+        ok = k0 + kk < kend;
+      } else {          // sub-tile [k][row]
         const int kk = c >> 4, row = (c & 15) * 8;
-        off = (row >> 5) * SUBT + kk * PITCH + (row & 31);
+        off = (row >> 5) * GSUB + swz16(kk, row & 31);
+        ok = k0 + kk < kend;
       }
-      *reinterpret_cast<V16*>(tile + off) = src[i];
+      *reinterpret_cast<V16*>(tile + off) = ok ? src[i] : (V16){0u, 0u, 0u, 0u};
     }
   };
   // operand of sub-tile s (32 rows of the tile): lane <-> row l32, contraction <-> k (c-map)
   auto operand = [&](const bf16* tile, int mode, int s) __attribute__((always_inline)) {
-    return mode == 0 ? lds_c_op(tile + s * SUBT + l32 * PITCH, g) : lds_tr_op<MAP_C>(tile + s * SUBT, PITCH, lane);
+    return mode == 0 ? swz_c_op(tile + s * GSUB, l32, g) : swz_tr_op_c(tile + s * GSUB, lane);
   };
 
   f32x16 acc[2][2];
@@ -125,18 +136,13 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     for (int j = 0; j < 2; j++) acc[i][j] = zero16();
 
   const long long yrows = a.N;  // K-major Y: rows n (a multiple of 128, never masked in practice)
-  load(X, a.ldx, XM, m0, a.M, kbeg, px);
-  load(Y, a.ldy, YM, n0, yrows, kbeg, py);
-  stash(sX[0], XM, px);
-  stash(sY[0], YM, py);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt++) {
-    const int b = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load(X, a.ldx, XM, m0, a.M, kbeg + (long long)(kt + 1) * BK, px);
-      load(Y, a.ldy, YM, n0, yrows, kbeg + (long long)(kt + 1) * BK, py);
-    }
+  // step kt: (clamped past the end: its data is never used)
+  auto kstart = [&](int kt) __attribute__((always_inline)) { return kbeg + (long long)min(kt, nk - 1) * BK; };
+  auto fetch = [&](int kt, int set) __attribute__((always_inline)) {
+    load(X, a.ldx, XM, m0, a.M, kstart(kt), px[set]);
+    load(Y, a.ldy, YM, n0, yrows, kstart(kt), py[set]);
+  };
+  auto compute = [&](int b) __attribute__((always_inline)) {
     Op<bf16> xo[2], yo[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) xo[i] = operand(sX[b], XM, 2 * wm + i);
@@ -146,12 +152,32 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < 2; i++)
 #pragma unroll
       for (int j = 0; j < 2; j++) acc[i][j] = mma32(yo[j], xo[i], acc[i][j]);  // D^T: lane = m, registers = n
-    if (more) {
-      stash(sX[b ^ 1], XM, px);
-      stash(sY[b ^ 1], YM, py);
+  };
+  fetch(0, 0);
+  fetch(1, 1);
+  stash(sX[0], XM, px[0], kstart(0));
+  stash(sY[0], YM, py[0], kstart(0));
+  __syncthreads();
+  // Two steps per iteration (set and buffer 0, then 1): fetch step kt + 2 into
+  // the set just stored, compute step kt, store step kt + 1's set, barrier.
+  // An odd last step is left in buffer 0 for after the loop; fetches past the
+  // end are clamped (their data is never used).
+  int kt = 0;
+  for (; kt + 2 <= nk; kt += 2) {
+    fetch(kt + 2, 0);
+    compute(0);
+    stash(sX[1], XM, px[1], kstart(kt + 1));
+    stash(sY[1], YM, py[1], kstart(kt + 1));
+    __syncthreads();
+    fetch(kt + 3, 1);
+    compute(1);
+    if (kt + 2 < nk) {
+      stash(sX[0], XM, px[0], kstart(kt + 2));
+      stash(sY[0], YM, py[0], kstart(kt + 2));
     }
     __syncthreads();
   }
+  if (kt < nk) compute(0);
 
   // acc[i][j][r]: row m0 + 32 (2 wm + i) + l32, column n0 + 32 (2 wn + j) + mrow(g, r)
 #pragma unroll
